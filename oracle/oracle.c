@@ -1,0 +1,311 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for exact scaled-dot-product attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file: only the test suite, the smoke check and the
+ * benchmark's cpu_baseline leg use it.  It shares no code, header, table or
+ * constant with the HIP kernels.
+ *
+ * What it computes (written from the pages, not from any listing):
+ *
+ *   S   = scale * Q K^T                      [Online-softmax note "research-attention",
+ *   P   = row-wise softmax of S                 section 01, the three-line definition;
+ *   O   = P V                                   "Flash Attention" notes page, the
+ *                                               Attention(Q,K,V) formula]
+ *   LSE = m + ln(l), m the row max of S, l = sum_j exp(S_j - m)
+ *                                             [research-attention, section 04: saving
+ *                                               L = m + log(l) is enough to rebuild P]
+ *
+ *   Backward (page 1 "Flash Attention 原理与实现", section "Backward 的 Tiling
+ *   策略", lists dV = P^T dO, dP = dO V^T, dQ = dS K, dK = dS^T Q and leaves
+ *   the softmax gradient to the paper).  The softmax vector-Jacobian product
+ *   used here is the textbook one: for one row p = softmax(s) and upstream
+ *   gradient g = dP_row, ds_j = p_j (g_j - sum_k p_k g_k).  The scale lands on
+ *   dQ and dK by the chain rule, not on dV.
+ *
+ *   Causal mask: key j is allowed for query i exactly when j <= i (top-left
+ *   alignment, for any Nq and Nk).  Masked keys take no part in max, sum or
+ *   products; their probability is exactly 0.  Key 0 is always allowed, so
+ *   every row is non-empty.
+ *
+ * The oracle materialises S and P for a whole head in fp64 and uses libm
+ * exp/log.  Summation order is the plain ascending order of the index being
+ * summed; nothing is blocked, fused or reordered.
+ *
+ * oracle_online_row / oracle_tiled_fwd follow the running-state recurrence of
+ * research-attention section 02 (state m, l, u; merge with alpha = exp(m - m'),
+ * p_j = exp(s_j - m'); init (-inf, 0, 0); one division at the end), in the
+ * page's notation, for checking the tiled/untiled agreement and the worked
+ * row's intermediate state.
+ *
+ * All arrays are contiguous row-major: Q [B,H,Nq,d], K/V [B,H,Nk,d],
+ * O/dO/dQ [B,H,Nq,d], dK/dV [B,H,Nk,d], LSE [B,H,Nq].  Returns 0 on success,
+ * -1 on a bad argument, -2 if a scratch allocation fails.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static int allowed(int64_t i, int64_t j, int causal) { return !causal || j <= i; }
+
+static double dot(const double *a, const double *b, int64_t n) {
+    double acc = 0.0;
+    for (int64_t c = 0; c < n; ++c) acc += a[c] * b[c];
+    return acc;
+}
+
+static int bad_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
+    return B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0;
+}
+
+/* One head: S (scaled scores) then P in place, plus m, l, LSE per row. */
+static void head_probs(const double *Q, const double *K, int64_t Nq, int64_t Nk, int64_t d,
+                       double scale, int causal, double *P, double *LSE) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < Nq; ++i) {
+        double *row = P + i * Nk;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < Nk; ++j) {
+            if (allowed(i, j, causal)) {
+                row[j] = scale * dot(Q + i * d, K + j * d, d);
+                if (row[j] > m) m = row[j];
+            }
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < Nk; ++j)
+            if (allowed(i, j, causal)) l += exp(row[j] - m);
+        for (int64_t j = 0; j < Nk; ++j)
+            row[j] = allowed(i, j, causal) ? exp(row[j] - m) / l : 0.0;
+        LSE[i] = m + log(l);
+    }
+}
+
+/* O_i = sum_j P[i][j] V_j */
+static void head_pv(const double *P, const double *V, int64_t Nq, int64_t Nk, int64_t d, double *O) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < Nq; ++i) {
+        double *o = O + i * d;
+        for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+        for (int64_t j = 0; j < Nk; ++j) {
+            const double p = P[i * Nk + j];
+            for (int64_t c = 0; c < d; ++c) o[c] += p * V[j * d + c];
+        }
+    }
+}
+
+/*
+ * Forward over all heads.  P_out may be NULL; when given it receives the
+ * probabilities [B,H,Nq,Nk] (only sensible for small shapes).
+ */
+int oracle_fwd(const double *Q, const double *K, const double *V, int64_t B, int64_t H,
+               int64_t Nq, int64_t Nk, int64_t d, double scale, int causal,
+               double *O, double *LSE, double *P_out) {
+    if (!Q || !K || !V || !O || !LSE || bad_shape(B, H, Nq, Nk, d)) return -1;
+    double *P = (double *)malloc(sizeof(double) * (size_t)(Nq * Nk));
+    if (!P) return -2;
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const double *q = Q + bh * Nq * d, *k = K + bh * Nk * d, *v = V + bh * Nk * d;
+        head_probs(q, k, Nq, Nk, d, scale, causal, P, LSE + bh * Nq);
+        head_pv(P, v, Nq, Nk, d, O + bh * Nq * d);
+        if (P_out) memcpy(P_out + bh * Nq * Nk, P, sizeof(double) * (size_t)(Nq * Nk));
+    }
+    free(P);
+    return 0;
+}
+
+/*
+ * Forward for selected query rows only: rows[bh*nrows + r] is the r-th query
+ * row of head bh.  Each row's softmax runs over every allowed key, exactly as
+ * in oracle_fwd; O_rows is [B*H, nrows, d], LSE_rows is [B*H, nrows].
+ */
+int oracle_fwd_rows(const double *Q, const double *K, const double *V, int64_t B, int64_t H,
+                    int64_t Nq, int64_t Nk, int64_t d, double scale, int causal,
+                    const int64_t *rows, int64_t nrows, double *O_rows, double *LSE_rows) {
+    if (!Q || !K || !V || !rows || !O_rows || !LSE_rows || nrows < 0 || bad_shape(B, H, Nq, Nk, d))
+        return -1;
+    for (int64_t t = 0; t < B * H * nrows; ++t)
+        if (rows[t] < 0 || rows[t] >= Nq) return -1;
+    int err = 0;
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)Nk);
+        if (!s) {
+            #pragma omp atomic write
+            err = -2;
+        }
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < B * H * nrows; ++t) {
+            if (!s) continue;
+            const int64_t bh = t / nrows, i = rows[t];
+            const double *q = Q + (bh * Nq + i) * d, *k = K + bh * Nk * d, *v = V + bh * Nk * d;
+            double m = -INFINITY;
+            for (int64_t j = 0; j < Nk; ++j) {
+                if (allowed(i, j, causal)) {
+                    s[j] = scale * dot(q, k + j * d, d);
+                    if (s[j] > m) m = s[j];
+                }
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < Nk; ++j)
+                if (allowed(i, j, causal)) l += exp(s[j] - m);
+            double *o = O_rows + t * d;
+            for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+            for (int64_t j = 0; j < Nk; ++j) {
+                if (!allowed(i, j, causal)) continue;
+                const double p = exp(s[j] - m) / l;
+                for (int64_t c = 0; c < d; ++c) o[c] += p * v[j * d + c];
+            }
+            LSE_rows[t] = m + log(l);
+        }
+        free(s);
+    }
+    return err;
+}
+
+/*
+ * Backward over all heads.  Given Q, K, V and the upstream gradient dO,
+ * returns dQ, dK, dV (and, when non-NULL, O and LSE of the same forward).
+ * Per head: P as in the forward, dP = dO V^T, r_i = sum_j P_ij dP_ij,
+ * dS = P (dP - r), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.
+ */
+int oracle_bwd(const double *Q, const double *K, const double *V, const double *dO,
+               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, double scale, int causal,
+               double *dQ, double *dK, double *dV, double *O, double *LSE) {
+    if (!Q || !K || !V || !dO || !dQ || !dK || !dV || bad_shape(B, H, Nq, Nk, d)) return -1;
+    double *P = (double *)malloc(sizeof(double) * (size_t)(Nq * Nk));
+    double *dS = (double *)malloc(sizeof(double) * (size_t)(Nq * Nk));
+    double *lse = (double *)malloc(sizeof(double) * (size_t)Nq);
+    if (!P || !dS || !lse) {
+        free(P); free(dS); free(lse);
+        return -2;
+    }
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const double *q = Q + bh * Nq * d, *k = K + bh * Nk * d, *v = V + bh * Nk * d;
+        const double *go = dO + bh * Nq * d;
+        double *gq = dQ + bh * Nq * d, *gk = dK + bh * Nk * d, *gv = dV + bh * Nk * d;
+
+        head_probs(q, k, Nq, Nk, d, scale, causal, P, lse);
+        if (O) head_pv(P, v, Nq, Nk, d, O + bh * Nq * d);
+        if (LSE) memcpy(LSE + bh * Nq, lse, sizeof(double) * (size_t)Nq);
+
+        /* dP = dO V^T, then dS = P (dP - r) row by row */
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < Nq; ++i) {
+            double *row = dS + i * Nk;
+            for (int64_t j = 0; j < Nk; ++j) row[j] = dot(go + i * d, v + j * d, d);
+            double r = 0.0;
+            for (int64_t j = 0; j < Nk; ++j) r += P[i * Nk + j] * row[j];
+            for (int64_t j = 0; j < Nk; ++j) row[j] = P[i * Nk + j] * (row[j] - r);
+        }
+        /* dQ_i = scale sum_j dS_ij K_j */
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < Nq; ++i) {
+            double *g = gq + i * d;
+            for (int64_t c = 0; c < d; ++c) g[c] = 0.0;
+            for (int64_t j = 0; j < Nk; ++j) {
+                const double w = dS[i * Nk + j];
+                for (int64_t c = 0; c < d; ++c) g[c] += w * k[j * d + c];
+            }
+            for (int64_t c = 0; c < d; ++c) g[c] *= scale;
+        }
+        /* dK_j = scale sum_i dS_ij Q_i ; dV_j = sum_i P_ij dO_i */
+        #pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < Nk; ++j) {
+            double *a = gk + j * d, *b = gv + j * d;
+            for (int64_t c = 0; c < d; ++c) { a[c] = 0.0; b[c] = 0.0; }
+            for (int64_t i = 0; i < Nq; ++i) {
+                const double ws = dS[i * Nk + j], wp = P[i * Nk + j];
+                for (int64_t c = 0; c < d; ++c) {
+                    a[c] += ws * q[i * d + c];
+                    b[c] += wp * go[i * d + c];
+                }
+            }
+            for (int64_t c = 0; c < d; ++c) a[c] *= scale;
+        }
+    }
+    free(P); free(dS); free(lse);
+    return 0;
+}
+
+/*
+ * Running-state recurrence for one row (research-attention, section 02):
+ * scores s[0..n), value rows v[n][dv].  Processes the first `ntiles` tiles of
+ * `tile` consecutive scores (all of them when ntiles < 0) starting from the
+ * state (m, l, u) = (-inf, 0, 0), and returns that state unnormalised.
+ */
+int oracle_online_row(const double *s, const double *v, int64_t n, int64_t dv, int64_t tile,
+                      int64_t ntiles, double *m_out, double *l_out, double *u_out) {
+    if (!s || !v || !m_out || !l_out || !u_out || n <= 0 || dv <= 0 || tile <= 0) return -1;
+    double m = -INFINITY, l = 0.0;
+    for (int64_t c = 0; c < dv; ++c) u_out[c] = 0.0;
+    int64_t done = 0;
+    for (int64_t start = 0; start < n && (ntiles < 0 || done < ntiles); start += tile, ++done) {
+        const int64_t end = start + tile < n ? start + tile : n;
+        double block_max = -INFINITY;
+        for (int64_t j = start; j < end; ++j)
+            if (s[j] > block_max) block_max = s[j];
+        const double m_new = m > block_max ? m : block_max;
+        const double alpha = exp(m - m_new);
+        l *= alpha;
+        for (int64_t c = 0; c < dv; ++c) u_out[c] *= alpha;
+        for (int64_t j = start; j < end; ++j) {
+            const double p = exp(s[j] - m_new);
+            l += p;
+            for (int64_t c = 0; c < dv; ++c) u_out[c] += p * v[j * dv + c];
+        }
+        m = m_new;
+    }
+    *m_out = m;
+    *l_out = l;
+    return 0;
+}
+
+/*
+ * Tiled forward: every query row runs the running-state recurrence over its
+ * allowed keys in tiles of `tile` keys, then o = u / l and LSE = m + ln l.
+ */
+int oracle_tiled_fwd(const double *Q, const double *K, const double *V, int64_t B, int64_t H,
+                     int64_t Nq, int64_t Nk, int64_t d, double scale, int causal, int64_t tile,
+                     double *O, double *LSE) {
+    if (!Q || !K || !V || !O || !LSE || tile <= 0 || bad_shape(B, H, Nq, Nk, d)) return -1;
+    int err = 0;
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)Nk);
+        double *vv = (double *)malloc(sizeof(double) * (size_t)(Nk * d));
+        if (!s || !vv) {
+            #pragma omp atomic write
+            err = -2;
+        }
+        #pragma omp for schedule(static)
+        for (int64_t t = 0; t < B * H * Nq; ++t) {
+            if (!s || !vv) continue;
+            const int64_t bh = t / Nq, i = t % Nq;
+            const double *q = Q + t * d, *k = K + bh * Nk * d, *v = V + bh * Nk * d;
+            int64_t n = 0; /* gather the allowed keys, in order */
+            for (int64_t j = 0; j < Nk; ++j) {
+                if (!allowed(i, j, causal)) continue;
+                s[n] = scale * dot(q, k + j * d, d);
+                memcpy(vv + n * d, v + j * d, sizeof(double) * (size_t)d);
+                ++n;
+            }
+            double m, l;
+            oracle_online_row(s, vv, n, d, tile, -1, &m, &l, O + t * d);
+            for (int64_t c = 0; c < d; ++c) O[t * d + c] /= l;
+            LSE[t] = m + log(l);
+        }
+        free(s);
+        free(vv);
+    }
+    return err;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,56 @@
+"""Plant plausible mistakes in a copy of the oracle's C source, build each on
+the CPU, and require that every mutant fails at least one pin.  This shows
+the pins constrain every part of the oracle (scale, sign, index, mask,
+normalisation, recurrence), not just that the oracle passes them."""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, text in oracle.c, replacement)
+MUTANTS = [
+    ("dS_sign", "row[j] = P[i * Nk + j] * (row[j] - r);", "row[j] = P[i * Nk + j] * (row[j] + r);"),
+    ("r_without_P", "r += P[i * Nk + j] * row[j];", "r += row[j];"),
+    ("dQ_no_scale", "g[c] *= scale;", "g[c] *= 1.0;"),
+    ("dK_no_scale", "a[c] *= scale;", "a[c] *= 1.0;"),
+    ("dQ_uses_V", "g[c] += w * k[j * d + c];", "g[c] += w * v[j * d + c];"),
+    ("dK_uses_P", "ws = dS[i * Nk + j], wp", "ws = P[i * Nk + j], wp"),
+    ("dV_uses_dS", "wp = P[i * Nk + j];", "wp = dS[i * Nk + j];"),
+    ("dV_uses_Q", "b[c] += wp * go[i * d + c];", "b[c] += wp * q[i * d + c];"),
+    ("mask_reversed", "return !causal || j <= i;", "return !causal || j >= i;"),
+    ("mask_strict", "return !causal || j <= i;", "return !causal || j < i || j == 0;"),
+    ("no_scale_in_S", "row[j] = scale * dot(Q + i * d, K + j * d, d);", "row[j] = dot(Q + i * d, K + j * d, d);"),
+    ("sum_without_shift", "if (allowed(i, j, causal)) l += exp(row[j] - m);", "if (allowed(i, j, causal)) l += exp(row[j]);"),
+    ("lse_sign", "LSE[i] = m + log(l);", "LSE[i] = m - log(l);"),
+    ("online_l_not_rescaled", "    l *= alpha;\n", "    l *= 1.0;\n"),
+    ("online_u_not_rescaled", "u_out[c] *= alpha;", "u_out[c] *= 1.0;"),
+    ("online_alpha_sign", "const double alpha = exp(m - m_new);", "const double alpha = exp(m_new - m);"),
+    ("online_p_old_max", "const double p = exp(s[j] - m_new);", "const double p = exp(s[j] - m);"),
+    ("rows_no_mask", "if (!allowed(i, j, causal)) continue;\n                const double p", "const double p"),
+]
+
+
+def _build_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, (name, src.count(old))
+    mutant = tmp_path / ("oracle_%s.c" % name)
+    mutant.write_text(src.replace(old, new))
+    lib = tmp_path / ("liboracle_%s.so" % name)
+    oracle.compile_source(str(mutant), str(lib))
+    return oracle.Oracle(str(lib))
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    o = _build_mutant(tmp_path, name, old, new)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, FloatingPointError, RuntimeError, ValueError, ZeroDivisionError):
+            failed.append(pin.__name__)
+    assert failed, "mutant %s passed every pin" % name
