@@ -1,0 +1,112 @@
+/*
+ * fa.h -- C ABI of libfa: exact scaled-dot-product attention, computed the
+ * FlashAttention way, for AMD Instinct MI355X (gfx950).
+ *
+ * Operation (definition: lumenova.space "research-attention", section 01;
+ * the Attention(Q,K,V) formula of the jrdollar31.pages.dev "Flash Attention"
+ * notes), for every batch b and head h independently:
+ *
+ *     S   = scale * Q K^T                 Q: [Nq, d], K: [Nk, d]
+ *     P   = softmax over each row of S    (keys j > i removed when causal)
+ *     O   = P V                           V: [Nk, d], O: [Nq, d]
+ *     LSE = m + ln(l)  per query row, m = row max of S, l = sum_j exp(S_j - m)
+ *
+ * The forward never forms S or P in memory: it runs the running-state
+ * recurrence (m, l, unnormalised O) over key tiles (research-attention,
+ * section 02; page 1 "Flash Attention 原理与实现", section "Forward 的 Tiling
+ * 策略") and saves LSE, which is enough to rebuild P later
+ * (research-attention, section 04).  The backward recomputes P from Q, K and
+ * LSE (page 1, section "Backward 的 Tiling 策略") and returns
+ * dV = P^T dO, dQ = scale * dS K, dK = scale * dS^T Q with the softmax
+ * gradient dS = P * (dO V^T - rowsum(dO * O)).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are caller-owned DEVICE pointers, contiguous row-major
+ *    [B, H, N, d] (d fastest), base address 16-byte aligned.  LSE is
+ *    [B, H, Nq] float32, natural log, in units of the scaled scores.
+ *  - dtype selects the element type of Q, K, V, O, dO, dQ, dK, dV.
+ *    FA_F32 reads and writes float32 but rounds the matrix-core operands
+ *    (Q, K, V, dO, and the probabilities) to 16-bit first, so it is not a
+ *    true-fp32 attention.  Accumulation is float32 in every mode.
+ *  - causal != 0 keeps key j for query i exactly when j <= i (top-left
+ *    alignment, for any Nq and Nk).  Key 0 is always kept, so no row is empty.
+ *  - d must be 64 or 128.  B, H, Nq, Nk >= 1 need not be multiples of any
+ *    tile size.  B*H*max(Nq,Nk)*d must stay below 2^31 elements.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls only
+ *    enqueue work on it: they do not synchronise, allocate or keep state, and
+ *    may be called from several host threads.  fa_bwd must be ordered after
+ *    the fa_fwd that produced O and LSE (same stream, or an event).
+ *  - Errors: argument problems are detected on the host before anything is
+ *    enqueued and returned as FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED;
+ *    FA_ERR_HIP means a launch was rejected by the HIP runtime.  No entry
+ *    point aborts or throws across the ABI.
+ */
+#ifndef LIBFA_FA_H
+#define LIBFA_FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, size <= 0, scale not finite and > 0, workspace too small */
+    FA_ERR_UNSUPPORTED = 2, /* head dim or dtype this build has no kernel for, size too large */
+    FA_ERR_HIP = 3          /* the HIP runtime rejected a launch */
+} fa_status;
+
+typedef enum fa_dtype {
+    FA_BF16 = 0,
+    FA_F16 = 1,
+    FA_F32 = 2
+} fa_dtype;
+
+/*
+ * Forward.  Reads Q [B,H,Nq,d], K [B,H,Nk,d], V [B,H,Nk,d]; writes
+ * O [B,H,Nq,d] (dtype) and LSE [B,H,Nq] (float32).  `scale` multiplies
+ * Q K^T before masking and softmax (1/sqrt(d) in the usual definition); it
+ * must be finite and positive.  O and LSE must not overlap the inputs.
+ */
+fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                 int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                 int dtype, void *stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for this shape: a float32 row
+ * statistic D = rowsum(dO * O) [B,H,Nq] and a float32 dQ accumulator
+ * [B,H,Nq,d], each padded to 256 bytes.  Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d);
+
+/*
+ * Backward.  Reads Q, K, V, the forward's O and LSE, and the upstream
+ * gradient dO [B,H,Nq,d]; writes dQ [B,H,Nq,d], dK and dV [B,H,Nk,d]
+ * (dtype).  `workspace` is caller-owned device memory of at least
+ * fa_bwd_workspace_size() bytes, 256-byte aligned; its contents on entry
+ * do not matter and on return are unspecified.  Same scale/causal/dtype as
+ * the forward.  dQ is accumulated with float32 atomics, so its low bits may
+ * differ from run to run; dK and dV are deterministic.
+ */
+fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                 const float *LSE, void *dQ, void *dK, void *dV,
+                 int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, human-readable name of a status code ("FA_OK", ...). */
+const char *fa_status_string(int status);
+
+/*
+ * Description of the kernels fa_fwd / fa_bwd would launch for this
+ * head dim, dtype and mask (kernel names, tile sizes, waves per workgroup),
+ * or "unsupported".  The string lives in thread-local storage and stays
+ * valid until the same thread calls fa_describe again.
+ */
+const char *fa_describe(int d, int dtype, int causal);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFA_FA_H */

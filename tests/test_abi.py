@@ -1,0 +1,113 @@
+"""The C ABI on the host: the library loads, exports every symbol include/fa.h
+declares, and rejects bad arguments before touching the GPU (CPU only; no
+call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_online_softmax_03_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert names == ["fa_bwd", "fa_bwd_workspace_size", "fa_describe", "fa_fwd", "fa_status_string"]
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert fa.fa_status_string(0) == "FA_OK"
+    assert fa.fa_status_string(1) == "FA_ERR_INVALID_ARG"
+    assert fa.fa_status_string(2) == "FA_ERR_UNSUPPORTED"
+    assert fa.fa_status_string(3) == "FA_ERR_HIP"
+    assert fa.fa_status_string(99) == "FA_UNKNOWN_STATUS"
+
+
+def test_describe(lib):
+    for d in (64, 128):
+        for dt in (0, 1, 2):
+            for c in (0, 1):
+                s = fa.fa_describe(d, dt, c)
+                assert "fwd" in s and "bwd" in s and ("d=%d" % d) in s
+    assert fa.fa_describe(96, 0, 0) == "unsupported"
+    assert fa.fa_describe(64, 7, 0) == "unsupported"
+
+
+def test_workspace_size(lib):
+    B, H, Nq, Nk, d = 2, 3, 100, 50, 64
+    rows = B * H * Nq
+    pad = lambda n: (n + 255) // 256 * 256
+    assert fa.fa_bwd_workspace_size(B, H, Nq, Nk, d) == pad(rows * 4) + pad(rows * d * 4)
+    assert fa.fa_bwd_workspace_size(0, H, Nq, Nk, d) == 0
+    assert fa.fa_bwd_workspace_size(B, H, Nq, -1, d) == 0
+
+
+# Fake, aligned, never-dereferenced addresses: every case below fails validation.
+P = ctypes.c_void_p(0x10000)
+MIS = ctypes.c_void_p(0x10008)
+NULL = ctypes.c_void_p(0)
+
+
+def _fwd(lib, Q=P, O=P, B=1, H=1, Nq=8, Nk=8, d=64, scale=0.125, dtype=0):
+    return lib.fa_fwd(Q, P, P, O, P, B, H, Nq, Nk, d, scale, 0, dtype, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=NULL), fa.FA_ERR_INVALID_ARG),
+    (dict(O=NULL), fa.FA_ERR_INVALID_ARG),
+    (dict(Q=MIS), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-0.5), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 14, H=1 << 10, Nq=1 << 10), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fwd_rejects(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+
+
+def _bwd(lib, ws=P, ws_bytes=1 << 40, dQ=P, d=64, dtype=0, Nq=8):
+    return lib.fa_bwd(P, P, P, P, P, P, dQ, P, P, 1, 1, Nq, 8, d, 0.125, 0, dtype, ws, ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=NULL), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=ctypes.c_void_p(0x10010)), fa.FA_ERR_INVALID_ARG),  # not 256-byte aligned
+    (dict(ws_bytes=16), fa.FA_ERR_INVALID_ARG),
+    (dict(dQ=NULL), fa.FA_ERR_INVALID_ARG),
+    (dict(dQ=MIS), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=-1), fa.FA_ERR_UNSUPPORTED),
+])
+def test_bwd_rejects(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    Q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(Q, Q, Q)

@@ -1,0 +1,164 @@
+"""Python binding of libfa, the gfx950 attention library (include/fa.h).
+
+Argument marshalling only: torch tensors supply device memory and the HIP
+stream, every step of the computation runs in the library's HIP kernels.
+There is no fallback: if libfa.so is missing or fails to load, every call
+raises.
+
+Entry points keep the C names:
+
+    fa_fwd(Q, K, V, O, LSE, scale, causal=False, stream=None)
+    fa_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal=False, stream=None)
+    fa_bwd_workspace_size(B, H, Nq, Nk, d) -> int
+    fa_status_string(status) -> str
+    fa_describe(d, dtype, causal) -> str
+
+plus ``forward`` / ``backward`` helpers that allocate the outputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_BF16, FA_F16, FA_F32 = 0, 1, 2
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s returned %s (%d)" % (what, fa_status_string(status), status))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libfa.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    L.fa_fwd.restype = i
+    L.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
+    L.fa_bwd_workspace_size.restype = sz
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    L.fa_bwd.restype = i
+    L.fa_status_string.argtypes = [i]
+    L.fa_status_string.restype = ctypes.c_char_p
+    L.fa_describe.argtypes = [i, i, i]
+    L.fa_describe.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def dtype_code(t) -> int:
+    import torch
+    codes = {torch.bfloat16: FA_BF16, torch.float16: FA_F16, torch.float32: FA_F32}
+    if t not in codes:
+        raise ValueError("unsupported dtype %s" % t)
+    return codes[t]
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dims(Q, K):
+    if Q.dim() != 4 or K.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    B, H, Nq, d = Q.shape
+    return B, H, Nq, K.shape[2], d
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def fa_fwd(Q, K, V, O, LSE, scale=None, causal=False, stream=None) -> None:
+    B, H, Nq, Nk, d = _dims(Q, K)
+    for t in (Q, K, V, O, LSE):
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    _need(K.shape == V.shape and O.shape == Q.shape and tuple(LSE.shape) == (B, H, Nq), "shape mismatch")
+    _need(Q.dtype == K.dtype == V.dtype == O.dtype, "Q, K, V, O must share a dtype")
+    _need(str(LSE.dtype) == "torch.float32", "LSE must be float32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, H, Nq, Nk, d, float(scale),
+                      int(bool(causal)), dtype_code(Q.dtype), _stream_handle(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd")
+
+
+def fa_bwd_workspace_size(B, H, Nq, Nk, d) -> int:
+    return int(lib().fa_bwd_workspace_size(B, H, Nq, Nk, d))
+
+
+def fa_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale=None, causal=False, stream=None) -> None:
+    B, H, Nq, Nk, d = _dims(Q, K)
+    for t in (Q, K, V, O, dO, LSE, dQ, dK, dV, workspace):
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    _need(K.shape == V.shape == dK.shape == dV.shape and Q.shape == O.shape == dO.shape == dQ.shape,
+          "shape mismatch")
+    _need(len({Q.dtype, K.dtype, V.dtype, O.dtype, dO.dtype, dQ.dtype, dK.dtype, dV.dtype}) == 1,
+          "all tensors except LSE and workspace must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib().fa_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV),
+                      B, H, Nq, Nk, d, float(scale), int(bool(causal)), dtype_code(Q.dtype), _ptr(workspace),
+                      nbytes, _stream_handle(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+
+
+def fa_status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def fa_describe(d: int, dtype: int, causal: bool) -> str:
+    return lib().fa_describe(int(d), int(dtype), int(bool(causal))).decode()
+
+
+# ------------------------------------------------------------------ helpers
+
+def forward(Q, K, V, scale=None, causal=False, stream=None):
+    """Allocate O and LSE, run fa_fwd, return (O, LSE)."""
+    import torch
+    B, H, Nq, Nk, d = _dims(Q, K)
+    O = torch.empty_like(Q)
+    LSE = torch.empty((B, H, Nq), device=Q.device, dtype=torch.float32)
+    fa_fwd(Q, K, V, O, LSE, scale, causal, stream)
+    return O, LSE
+
+
+def alloc_workspace(Q, K):
+    import torch
+    B, H, Nq, Nk, d = _dims(Q, K)
+    n = fa_bwd_workspace_size(B, H, Nq, Nk, d)
+    return torch.empty(n, device=Q.device, dtype=torch.uint8)
+
+
+def backward(Q, K, V, O, dO, LSE, scale=None, causal=False, stream=None, workspace=None):
+    """Allocate dQ, dK, dV (and the workspace unless given), run fa_bwd."""
+    import torch
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    if workspace is None:
+        workspace = alloc_workspace(Q, K)
+    fa_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal, stream)
+    return dQ, dK, dV

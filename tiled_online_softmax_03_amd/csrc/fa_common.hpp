@@ -1,0 +1,139 @@
+// fa_common.hpp -- device helpers shared by the libfa kernels (gfx950 only).
+//
+// Matrix-core conventions used throughout (CDNA3/CDNA4 32x32 MFMA, wave64):
+//   v_mfma_f32_32x32x16_{bf16,f16}: D[32x32] += A[32x16] * B[16x32]
+//   A operand: lane l holds A[row = l%32][k in slot (l/32, v)], v = 0..7
+//   B operand: lane l holds B[k in slot (l/32, v)][col = l%32]
+//   C/D      : lane l, register r (0..15) holds D[8*(r/4) + 4*(l/32) + r%4][l%32]
+// The contraction index k only has to be assigned to the same (l/32, v) slot
+// in A and B, so the kernels pick whatever k order makes their loads cheap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Element type of the tensors crossing the ABI.
+enum Elt : int { ELT_BF16 = 0, ELT_F16 = 1, ELT_F32 = 2 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16_t mfma_bf16(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma_f16(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// The 16-bit operand type of a matrix product on data of element type E:
+// fp16 data stays fp16, bf16 stays bf16, fp32 is rounded to bf16.
+template <int E>
+__device__ __forceinline__ f32x16_t mfma_in(u32x4_t a, u32x4_t b, f32x16_t c) {
+    if constexpr (E == ELT_F16) return mfma_f16(a, b, c);
+    else return mfma_bf16(a, b, c);
+}
+
+// Round-to-nearest-even packing of two floats (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    f32x2_t x = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+}
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+    f32x2_t x = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2_t));
+}
+template <int E>
+__device__ __forceinline__ uint32_t pack_in(float a, float b) {
+    if constexpr (E == ELT_F16) return pack_f16(a, b);
+    else return pack_bf16(a, b);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t u) {
+    return (float)__builtin_bit_cast(f16x2_t, u)[0];
+}
+__device__ __forceinline__ float f16_hi(uint32_t u) {
+    return (float)__builtin_bit_cast(f16x2_t, u)[1];
+}
+
+// Both halves' value combined: lanes l and l^32 exchange through
+// v_permlane32_swap; the two results are {own, partner} in some order.
+__device__ __forceinline__ float half_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Eight consecutive elements of an E-typed row as four 32-bit words of the
+// 16-bit MFMA operand type (fp32 is rounded to bf16 on the way).
+template <int E>
+__device__ __forceinline__ u32x4_t load8_operand(const void *base, int64_t elem) {
+    if constexpr (E == ELT_F32) {
+        const f32x4_t *p = reinterpret_cast<const f32x4_t *>(static_cast<const float *>(base) + elem);
+        f32x4_t a = p[0], b = p[1];
+        return u32x4_t{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(b[0], b[1]),
+                       pack_bf16(b[2], b[3])};
+    } else {
+        return *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(base) + elem);
+    }
+}
+
+// Eight consecutive elements of an E-typed row as floats.  fp32 data is first
+// rounded to bf16, the operand precision it is given everywhere else.
+template <int E>
+__device__ __forceinline__ void load8_float(const void *base, int64_t elem, float out[8]) {
+    if constexpr (E == ELT_F32) {
+        u32x4_t w = load8_operand<E>(base, elem);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { out[2 * i] = bf16_lo(w[i]); out[2 * i + 1] = bf16_hi(w[i]); }
+    } else {
+        u32x4_t w = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(base) + elem);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (E == ELT_BF16) { out[2 * i] = bf16_lo(w[i]); out[2 * i + 1] = bf16_hi(w[i]); }
+            else { out[2 * i] = f16_lo(w[i]); out[2 * i + 1] = f16_hi(w[i]); }
+        }
+    }
+}
+
+// Store four consecutive floats to an E-typed row (RNE for 16-bit types).
+template <int E>
+__device__ __forceinline__ void store4(void *base, int64_t elem, float a, float b, float c, float d) {
+    if constexpr (E == ELT_F32) {
+        *reinterpret_cast<f32x4_t *>(static_cast<float *>(base) + elem) = f32x4_t{a, b, c, d};
+    } else if constexpr (E == ELT_BF16) {
+        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(base) + elem) = u32x2_t{pack_bf16(a, b), pack_bf16(c, d)};
+    } else {
+        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(base) + elem) = u32x2_t{pack_f16(a, b), pack_f16(c, d)};
+    }
+}
+
+// Map a hardware workgroup index to a logical one so that consecutive
+// logical indices land on the same XCD.  Workgroups are handed to the eight
+// XCDs round-robin; this is a bijection on [0, n).
+__device__ __forceinline__ int xcd_remap(int p, int n) {
+    const int per = n / 8, rem = n % 8;
+    const int xcd = p % 8, slot = p / 8;
+    return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+}  // namespace fa

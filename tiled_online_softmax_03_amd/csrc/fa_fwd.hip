@@ -1,0 +1,247 @@
+// fa_fwd.hip -- attention forward for gfx950.
+//
+// Method: page 1 "Flash Attention 原理与实现", section "Forward 的 Tiling
+// 策略" (Q in row blocks, K/V streamed in key blocks, per-row running
+// statistics) with the single-exponential state update of lumenova.space
+// "research-attention", section 02 (m' = max(m, max s), alpha = exp(m - m'),
+// p = exp(s - m'), l' = alpha l + sum p, u' = alpha u + sum p v, one division
+// at the end) and LSE = m + ln l saved for the backward (same page, section 04).
+//
+// MI355X mapping (one workgroup = NW waves = 32*NW query rows of one head):
+//  * Each wave keeps its 32 query rows in VGPRs for the whole key loop.
+//  * K and V tiles of BC keys are staged through LDS, shared by all waves.
+//    K stays row-major (XOR-swizzled 16-byte chunks); V is written
+//    transposed and converted to fp16 while staging, so the P*V product reads
+//    it as an MFMA A operand with two 8-byte LDS reads.
+//  * Scores are formed transposed, S^T = K Q^T, so each lane owns one query
+//    row: the row max and row sum are in-lane reductions plus one
+//    permlane32 swap, and the rescale of the accumulator is one multiply per
+//    register with a lane-uniform factor.
+//  * O^T += V^T P^T runs on the fp16 matrix core: P is rounded to fp16
+//    (11-bit significand) rather than bf16, which keeps the output within a
+//    1e-3 relative-L2 budget; V converts from bf16 to fp16 exactly.
+//  * Softmax runs in base 2 with the scale folded into one FMA:
+//    p = exp2(s * scale*log2e - m2), m2 the running max in log2 units.
+#include "fa_common.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+
+// K tile in LDS: [BC][D] 16-bit, 16-byte chunk c of row r lives at chunk
+// c ^ kswz(r); chosen so 16 consecutive rows read at one chunk hit distinct
+// banks.
+template <int D>
+__device__ __forceinline__ int kswz(int row) { return (row / (128 / D)) % (D / 8); }
+
+// V^T tile in LDS: [D][BC] fp16, 8-byte unit u (4 keys) of row c lives at
+// unit u ^ vswz(c).
+template <int BC>
+__device__ __forceinline__ int vswz(int col) { return (col / (128 / BC)) % (BC / 4); }
+
+template <int D, int BC, int NW, int E, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
+                                                      const void *__restrict__ V, void *__restrict__ O,
+                                                      float *__restrict__ LSE, int BH, int Nq, int Nk,
+                                                      float scale_log2, int n_qt) {
+    constexpr int BR = 32 * NW;    // query rows per workgroup
+    constexpr int NT = NW * 64;    // threads
+    constexpr int NCH = D / 8;     // 16-byte chunks per K row
+    constexpr int NKB = BC / 32;   // 32-key blocks per tile
+    constexpr int NDB = D / 32;    // 32-column blocks of O
+    constexpr int NKS = D / 16;    // k-steps of the QK^T product
+    constexpr int NUNIT = BC / 4;  // 8-byte units per V^T row
+
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * BC];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, g = lane >> 5;
+
+    int bh, qt;
+    if constexpr (CAUSAL) {
+        // longest rows first: the last query tiles see the most keys
+        const int L = blockIdx.x;
+        qt = n_qt - 1 - L / BH;
+        bh = L % BH;
+    } else {
+        const int L = xcd_remap(blockIdx.x, gridDim.x);
+        bh = L / n_qt;
+        qt = L % n_qt;
+    }
+
+    const int64_t q_head = (int64_t)bh * Nq * D;
+    const int64_t k_head = (int64_t)bh * Nk * D;
+    const int q_wave0 = qt * BR + wave * 32;
+    const int q = q_wave0 + l32;  // this lane's query row
+    const int q_ld = q < Nq ? q : Nq - 1;
+
+    // Q^T fragments: B operand of S^T = K Q^T, k = head-dim index 16*ks + 8*g + v
+    u32x4_t qf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = load8_operand<E>(Q, q_head + (int64_t)q_ld * D + 16 * ks + 8 * g);
+
+    f32x16_t o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x16_t{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    int k_end = Nk;
+    if constexpr (CAUSAL) {
+        const int q_last = min(qt * BR + BR, Nq);  // one past the last query of the workgroup
+        k_end = min(Nk, q_last);
+    }
+    const int n_kt = (k_end + BC - 1) / BC;
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int k0 = kt * BC;
+        __syncthreads();  // previous tile fully consumed
+        // ---- stage K (row-major, swizzled) and V^T (fp16, swizzled)
+#pragma unroll
+        for (int i = tid; i < BC * NCH; i += NT) {
+            const int row = i / NCH, c = i % NCH;
+            u32x4_t w = {0u, 0u, 0u, 0u};
+            if (k0 + row < Nk) w = load8_operand<E>(K, k_head + (int64_t)(k0 + row) * D + c * 8);
+            *reinterpret_cast<u32x4_t *>(&Ks[row * D + ((c ^ kswz<D>(row)) * 8)]) = w;
+        }
+#pragma unroll
+        for (int i = tid; i < NUNIT * NCH; i += NT) {
+            const int c = i % NCH, u = i / NCH;  // keys 4u..4u+3, columns 8c..8c+7
+            float v[4][8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int key = k0 + 4 * u + k;
+                if (key < Nk) {
+                    load8_float<E>(V, k_head + (int64_t)key * D + c * 8, v[k]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[k][e] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int col = c * 8 + e;
+                *reinterpret_cast<u32x2_t *>(&Vt[col * BC + ((u ^ vswz<BC>(col)) * 4)]) =
+                    u32x2_t{pack_f16(v[0][e], v[1][e]), pack_f16(v[2][e], v[3][e])};
+            }
+        }
+        __syncthreads();
+
+        if (CAUSAL && k0 > q_wave0 + 31) continue;  // tile lies above the diagonal for every row of this wave
+
+        // ---- S^T = K Q^T : lane = query, register r -> key 8*(r/4) + 4*g + r%4 of each 32-key block
+        f32x16_t s[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            s[kb] = f32x16_t{};
+            const int row = kb * 32 + l32;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&Ks[row * D + (((2 * ks + g) ^ kswz<D>(row)) * 8)]);
+                s[kb] = mfma_in<E>(a, qf[ks], s[kb]);
+            }
+        }
+
+        const bool ragged = k0 + BC > Nk;
+        const bool diag = CAUSAL && (k0 + BC - 1 > q_wave0);
+        if (ragged || diag) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + kb * 32 + 8 * (r / 4) + 4 * g + (r % 4);
+                    if (key >= Nk || (CAUSAL && key > q)) s[kb][r] = -INFINITY;
+                }
+        }
+
+        // ---- running max / rescale / exponentials / running sum
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = half_max(mx);
+        const float m_new = fmaxf(m_run, mx * scale_log2);  // scale > 0, so max commutes with it
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+
+        uint32_t pk[NKB][8];
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i], scale_log2, -m_new));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i + 1], scale_log2, -m_new));
+                lsum += p0 + p1;
+                pk[kb][i] = pack_f16(p0, p1);
+            }
+        l_run += lsum;
+
+        // ---- O^T += V^T P^T (fp16 matrix core).  k-step kst covers keys
+        // 16*kst .. 16*kst+15; slot (g, v) holds key 16*kst + 4g + v (v < 4)
+        // or 16*kst + 8 + 4g + (v-4), matching the S^T register order.
+#pragma unroll
+        for (int kst = 0; kst < BC / 16; ++kst) {
+            const int kb = kst / 2, h = kst % 2;
+            const u32x4_t b = {pk[kb][4 * h], pk[kb][4 * h + 1], pk[kb][4 * h + 2], pk[kb][4 * h + 3]};
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int col = db * 32 + l32;
+                const int sw = vswz<BC>(col);
+                const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(&Vt[col * BC + (((4 * kst + g) ^ sw) * 4)]);
+                const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(&Vt[col * BC + (((4 * kst + 2 + g) ^ sw) * 4)]);
+                o[db] = mfma_f16(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, b, o[db]);
+            }
+        }
+    }
+
+    // ---- epilogue: O = u / l, LSE = (m2 + log2 l) * ln 2
+    const float l_tot = half_sum(l_run);
+    const float inv = 1.f / l_tot;
+    if (q < Nq) {
+        const int64_t orow = q_head + (int64_t)q * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq)
+                store4<E>(O, orow + db * 32 + 8 * rq + 4 * g, o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv,
+                          o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
+        if (g == 0) LSE[(int64_t)bh * Nq + q] = (m_run + __builtin_log2f(l_tot)) * kLn2;
+    }
+}
+
+template <int D, int E, bool CAUSAL>
+static hipError_t launch_fwd_t(const FwdArgs &a) {
+    constexpr int BC = 64, NW = 4, BR = 32 * NW;
+    const int n_qt = (a.Nq + BR - 1) / BR;
+    const int BH = a.B * a.H;
+    const dim3 grid(BH * n_qt), block(NW * 64);
+    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, E, CAUSAL>), grid, block, 0, (hipStream_t)a.stream, a.Q, a.K, a.V,
+                       a.O, a.LSE, BH, a.Nq, a.Nk, a.scale * kLog2e, n_qt);
+    return hipGetLastError();
+}
+
+template <int D, int E>
+static hipError_t launch_fwd_c(const FwdArgs &a) {
+    return a.causal ? launch_fwd_t<D, E, true>(a) : launch_fwd_t<D, E, false>(a);
+}
+
+template <int D>
+static hipError_t launch_fwd_d(const FwdArgs &a) {
+    switch (a.dtype) {
+        case ELT_BF16: return launch_fwd_c<D, ELT_BF16>(a);
+        case ELT_F16: return launch_fwd_c<D, ELT_F16>(a);
+        default: return launch_fwd_c<D, ELT_F32>(a);
+    }
+}
+
+hipError_t launch_fwd(const FwdArgs &a) { return a.d == 64 ? launch_fwd_d<64>(a) : launch_fwd_d<128>(a); }
+
+const char *describe_fwd() { return "fwd_kernel<D, BC=64, waves=4 (128 query rows), S^T=KQ^T bf16/f16 MFMA 32x32x16, PV fp16 MFMA>"; }
+
+}  // namespace fa
