@@ -1,0 +1,194 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = fa_fwd followed by fa_bwd (its three stages, launched one by one
+so each kernel can be timed with HIP events on the stream it runs on) over
+one batch of seeded synthetic inputs already resident in HBM.  The default
+workload is B=8, H=32, Nq=Nk=4096, d=128, bf16, non-causal.
+
+Prints ONE JSON line: whole-step throughput in TFLOP/s (forward counted as
+4*B*H*Nq*Nk*d, backward as 2.5x that), the forward alone, the per-kernel
+times, a roofline entry for the dominant kernel and a CPU baseline (the fp64
+oracle timed on a bounded sample of the same workload on this host).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+                    [--no-cpu-baseline] [--cpu-heads 8]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd & fwd+bwd TFLOP/s, % bf16 MFMA peak, at B8·H32·N4096·d128"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="train_b8h32n4096d128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=48, help="heads in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the attention path here runs on a single MI355X "
+              "(--gpus %d is not supported)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import tiled_online_softmax_03_amd as fa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    fa.lib()
+    w = synth.WORKLOADS[args.workload]
+    if not w.backward:
+        w = w.with_(backward=True)
+    dev = torch.device("cuda:0")
+    inp = synth.workload_inputs(w, device=dev, with_dO=True)
+    Q, K, V, dO = inp["Q"], inp["K"], inp["V"], inp["dO"]
+    O = torch.empty_like(Q)
+    LSE = torch.empty((w.B, w.H, w.Nq), device=dev, dtype=torch.float32)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    ws = fa.alloc_workspace(Q, K)
+    stream = torch.cuda.current_stream()
+    nst = fa.fa_bwd_num_stages()
+
+    def launch_step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        fa.fa_fwd(Q, K, V, O, LSE, w.scale, w.causal, stream)
+        if events is not None:
+            events[1].record(stream)
+        for s in range(nst):
+            fa.fa_bwd_stage(s, Q, K, V, O, dO, LSE, dQ, dK, dV, ws, w.scale, w.causal, stream)
+            if events is not None:
+                events[2 + s].record(stream)
+
+    for _ in range(args.warmup):
+        launch_step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + nst)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        launch_step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    peak_mem = torch.cuda.max_memory_allocated()
+
+    names = ["fwd_kernel"] + ["bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"][:nst]
+    per = {n: [] for n in names}
+    for e in evs:
+        for k, n in enumerate(names):
+            per[n].append(e[k].elapsed_time(e[k + 1]))
+    kern_ms = {n: sum(v) / len(v) for n, v in per.items()}
+    step_ms = (t1 - t0) * 1e3 / args.steps
+
+    F = w.fwd_flops()
+    total_flops = 3.5 * F
+    value = total_flops / (step_ms * 1e-3) / 1e12
+    fwd_tflops = F / (kern_ms["fwd_kernel"] * 1e-3) / 1e12
+    bwd_ms = sum(kern_ms[n] for n in names[1:])
+    bwd_tflops = 2.5 * F / (bwd_ms * 1e-3) / 1e12
+
+    # algorithmic work per launch of each kernel
+    elt = {"bf16": 2, "f16": 2, "f32": 4}[w.dtype]
+    rows = w.B * w.H * w.Nq
+    # (one matrix product of a head is 2*Nq*Nk*d flops = F/2 per head summed)
+    work = {
+        "fwd_kernel": ("mfma", F),                    # S, P V
+        "bwd_pre_kernel": ("hbm", 2 * rows * w.d * elt + rows * 4),  # read O, dO; write D
+        "bwd_dkdv_kernel": ("mfma", 2.0 * F),         # S, dP, dV, dK
+        "bwd_dq_kernel": ("mfma", 1.5 * F),           # S, dP, dQ
+    }
+    dom = max(names, key=lambda n: kern_ms[n])
+    bound, units = work[dom]
+    if bound == "mfma":
+        achieved = units / (kern_ms[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "flops_per_launch": units, "avg_launch_ms": kern_ms[dom]}
+    else:
+        achieved = units / (kern_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": units,
+                "avg_launch_ms": kern_ms[dom]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inp, args.cpu_heads)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "step": "fa_fwd + fa_bwd"},
+        "fwd_tflops": fwd_tflops,
+        "fwd_pct_peak": 100.0 * fwd_tflops / PEAK_BF16_TFLOPS,
+        "bwd_tflops": bwd_tflops,
+        "fwd_bwd_pct_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "kernel_ms": kern_ms,
+        "peak_mem_bytes": peak_mem,
+        "describe": fa.fa_describe(w.d, fa.dtype_code(w.torch_dtype), w.causal),
+        "device": torch.cuda.get_device_properties(0).gcnArchName,
+        "torch": torch.__version__,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, inp, heads):
+    """The fp64 oracle (fwd + analytic bwd, untiled) on the first `heads`
+    heads of the same inputs, timed on this host's cores."""
+    import oracle
+
+    BH = w.B * w.H
+    heads = max(1, min(heads, BH))
+    views = {}
+    for k in ("Q", "K", "V", "dO"):
+        t = inp[k].reshape(BH, 1, inp[k].shape[2], w.d)[:heads]
+        t = t.to("cpu")
+        if t.dtype == __import__("torch").float32:
+            t = t.to(__import__("torch").bfloat16)
+        views[k] = t.double().numpy()
+    o = oracle.load()
+    t0 = time.perf_counter()
+    o.bwd(views["Q"], views["K"], views["V"], views["dO"], w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    flops = heads * 3.5 * w.fwd_flops() / BH
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": o.num_threads(), "kind": "oracle",
+            "sample": "%d of %d heads of %s, forward + backward, fp64, %.2f s" % (heads, BH, w.name, dt)}
+
+
+if __name__ == "__main__":
+    main()

@@ -74,9 +74,9 @@ fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LS
                  int dtype, void *stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for this shape: a float32 row
- * statistic D = rowsum(dO * O) [B,H,Nq] and a float32 dQ accumulator
- * [B,H,Nq,d], each padded to 256 bytes.  Returns 0 for invalid sizes.
+ * Bytes of device workspace fa_bwd needs for this shape: the float32 row
+ * statistic D = rowsum(dO * O) [B,H,Nq], padded to 256 bytes.  Returns 0
+ * for invalid sizes.
  */
 size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d);
 
@@ -86,13 +86,30 @@ size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d);
  * (dtype).  `workspace` is caller-owned device memory of at least
  * fa_bwd_workspace_size() bytes, 256-byte aligned; its contents on entry
  * do not matter and on return are unspecified.  Same scale/causal/dtype as
- * the forward.  dQ is accumulated with float32 atomics, so its low bits may
- * differ from run to run; dK and dV are deterministic.
+ * the forward.  No atomics are used: dQ, dK and dV are bitwise
+ * reproducible for a given input, launch and device.
  */
 fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, const void *dO,
                  const float *LSE, void *dQ, void *dK, void *dV,
                  int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fa_bwd split into its kernel launches, for callers that schedule or time
+ * them one by one.  fa_bwd_num_stages() returns the number of stages;
+ * running fa_bwd_stage(0..n-1, ...) in order on one stream, with the same
+ * arguments and workspace, is exactly fa_bwd.  Stage 0 computes
+ * D = rowsum(dO * O) into the workspace, stage 1 is the K/V-stationary pass
+ * that writes dK and dV, stage 2 the Q-stationary pass that writes dQ
+ * (stages 1 and 2 both read D).  Same argument checks as fa_bwd; an unknown
+ * stage returns FA_ERR_INVALID_ARG.
+ */
+int fa_bwd_num_stages(void);
+
+fa_status fa_bwd_stage(int stage, const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                       const float *LSE, void *dQ, void *dK, void *dV,
+                       int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, human-readable name of a status code ("FA_OK", ...). */
 const char *fa_status_string(int status);

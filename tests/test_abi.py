@@ -25,7 +25,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert names == ["fa_bwd", "fa_bwd_workspace_size", "fa_describe", "fa_fwd", "fa_status_string"]
+    assert names == ["fa_bwd", "fa_bwd_num_stages", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_describe",
+                     "fa_fwd", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -52,7 +53,7 @@ def test_workspace_size(lib):
     B, H, Nq, Nk, d = 2, 3, 100, 50, 64
     rows = B * H * Nq
     pad = lambda n: (n + 255) // 256 * 256
-    assert fa.fa_bwd_workspace_size(B, H, Nq, Nk, d) == pad(rows * 4) + pad(rows * d * 4)
+    assert fa.fa_bwd_workspace_size(B, H, Nq, Nk, d) == pad(rows * 4)
     assert fa.fa_bwd_workspace_size(0, H, Nq, Nk, d) == 0
     assert fa.fa_bwd_workspace_size(B, H, Nq, -1, d) == 0
 
@@ -111,3 +112,12 @@ def test_binding_refuses_cpu_tensors():
     Q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.forward(Q, Q, Q)
+
+
+def test_bwd_stages(lib):
+    assert fa.fa_bwd_num_stages() == 3
+    args = (P, P, P, P, P, P, P, P, P, 1, 1, 8, 8, 64, 0.125, 0, 0, P, 1 << 40, NULL)
+    assert lib.fa_bwd_stage(3, *args) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_bwd_stage(-1, *args) == fa.FA_ERR_INVALID_ARG
+    bad = (P, P, P, P, P, P, NULL, P, P, 1, 1, 8, 8, 64, 0.125, 0, 0, P, 1 << 40, NULL)
+    assert lib.fa_bwd_stage(1, *bad) == fa.FA_ERR_INVALID_ARG

@@ -102,10 +102,21 @@ def test_workload_train():
     assert dK_sum.abs().max().item() <= 0.05 * dK.float().abs().sum(2).max().item()
 
 
-def test_dkdv_deterministic():
+def test_bwd_deterministic():
     inp = synth.make_inputs(2, 2, 300, 260, 128, "bf16", 9, device="cuda")
     _, _, dQ1, dK1, dV1 = _run(inp, 0.1, False)
     for _ in range(3):
         _, _, dQ2, dK2, dV2 = _run(inp, 0.1, False)
-        assert torch.equal(dK1, dK2) and torch.equal(dV1, dV2)
-        assert (dQ1.float() - dQ2.float()).abs().max().item() <= 1e-2
+        assert torch.equal(dK1, dK2) and torch.equal(dV1, dV2) and torch.equal(dQ1, dQ2)
+
+
+def test_stages_equal_fa_bwd():
+    """fa_bwd_stage(0..n-1) in order is exactly fa_bwd."""
+    inp = synth.make_inputs(1, 3, 333, 200, 64, "f16", 11, device="cuda")
+    O, LSE, dQ, dK, dV = _run(inp, 0.125, True)
+    ws = fa.alloc_workspace(inp["Q"], inp["K"])
+    sQ, sK, sV = torch.empty_like(dQ), torch.empty_like(dK), torch.empty_like(dV)
+    for st in range(fa.fa_bwd_num_stages()):
+        fa.fa_bwd_stage(st, inp["Q"], inp["K"], inp["V"], O, inp["dO"], LSE, sQ, sK, sV, ws, 0.125, True)
+    torch.cuda.synchronize()
+    assert torch.equal(sQ, dQ) and torch.equal(sK, dK) and torch.equal(sV, dV)

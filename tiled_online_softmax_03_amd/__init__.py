@@ -10,6 +10,8 @@ Entry points keep the C names:
     fa_fwd(Q, K, V, O, LSE, scale, causal=False, stream=None)
     fa_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal=False, stream=None)
     fa_bwd_workspace_size(B, H, Nq, Nk, d) -> int
+    fa_bwd_num_stages() -> int
+    fa_bwd_stage(stage, <fa_bwd arguments>)
     fa_status_string(status) -> str
     fa_describe(d, dtype, causal) -> str
 
@@ -51,6 +53,10 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_workspace_size.restype = sz
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     L.fa_bwd.restype = i
+    L.fa_bwd_num_stages.argtypes = []
+    L.fa_bwd_num_stages.restype = i
+    L.fa_bwd_stage.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    L.fa_bwd_stage.restype = i
     L.fa_status_string.argtypes = [i]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_describe.argtypes = [i, i, i]
@@ -109,7 +115,7 @@ def fa_bwd_workspace_size(B, H, Nq, Nk, d) -> int:
     return int(lib().fa_bwd_workspace_size(B, H, Nq, Nk, d))
 
 
-def fa_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale=None, causal=False, stream=None) -> None:
+def _bwd_args(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal, stream):
     B, H, Nq, Nk, d = _dims(Q, K)
     for t in (Q, K, V, O, dO, LSE, dQ, dK, dV, workspace):
         _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
@@ -120,11 +126,26 @@ def fa_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale=None, causal=False,
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     nbytes = workspace.numel() * workspace.element_size()
-    st = lib().fa_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV),
-                      B, H, Nq, Nk, d, float(scale), int(bool(causal)), dtype_code(Q.dtype), _ptr(workspace),
-                      nbytes, _stream_handle(stream))
+    return (_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV),
+            B, H, Nq, Nk, d, float(scale), int(bool(causal)), dtype_code(Q.dtype), _ptr(workspace), nbytes,
+            _stream_handle(stream))
+
+
+def fa_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale=None, causal=False, stream=None) -> None:
+    st = lib().fa_bwd(*_bwd_args(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal, stream))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+
+
+def fa_bwd_num_stages() -> int:
+    return int(lib().fa_bwd_num_stages())
+
+
+def fa_bwd_stage(stage, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale=None, causal=False, stream=None) -> None:
+    st = lib().fa_bwd_stage(int(stage), *_bwd_args(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal,
+                                                   stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_stage")
 
 
 def fa_status_string(status: int) -> str:

@@ -32,6 +32,8 @@ fa_status check_common(int B, int H, int Nq, int Nk, int d, float scale, int dty
 
 extern "C" {
 
+size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d);
+
 fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H, int Nq,
                  int Nk, int d, float scale, int causal, int dtype, void *stream) {
     if (!Q || !K || !V || !O || !LSE) return FA_ERR_INVALID_ARG;
@@ -46,12 +48,13 @@ fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LS
 size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d) {
     if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
     const size_t rows = (size_t)B * H * Nq;
-    return pad256(rows * sizeof(float)) + pad256(rows * (size_t)d * sizeof(float));
+    return pad256(rows * sizeof(float));
 }
 
-fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, const void *dO, const float *LSE,
-                 void *dQ, void *dK, void *dV, int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                 int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+static fa_status bwd_impl(int stage, const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                          const float *LSE, void *dQ, void *dK, void *dV, int B, int H, int Nq, int Nk, int d,
+                          float scale, int causal, int dtype, void *workspace, size_t workspace_bytes,
+                          void *stream) {
     if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV || !workspace) return FA_ERR_INVALID_ARG;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(LSE) ||
         !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
@@ -60,12 +63,26 @@ fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, con
     const fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
     if (st != FA_OK) return st;
     if (workspace_bytes < fa_bwd_workspace_size(B, H, Nq, Nk, d)) return FA_ERR_INVALID_ARG;
-    const size_t rows = (size_t)B * H * Nq;
     float *Dvec = static_cast<float *>(workspace);
-    float *dQacc = reinterpret_cast<float *>(static_cast<char *>(workspace) + pad256(rows * sizeof(float)));
-    fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal ? 1 : 0, dtype, Dvec, dQacc,
-                  stream};
-    return fa::launch_bwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+    fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal ? 1 : 0, dtype, Dvec, stream};
+    return fa::launch_bwd(a, stage) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, const void *dO, const float *LSE,
+                 void *dQ, void *dK, void *dV, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                 int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return bwd_impl(-1, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal, dtype, workspace,
+                    workspace_bytes, stream);
+}
+
+int fa_bwd_num_stages(void) { return fa::kBwdStages; }
+
+fa_status fa_bwd_stage(int stage, const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                       const float *LSE, void *dQ, void *dK, void *dV, int B, int H, int Nq, int Nk, int d,
+                       float scale, int causal, int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    if (stage < 0 || stage >= fa::kBwdStages) return FA_ERR_INVALID_ARG;
+    return bwd_impl(stage, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal, dtype, workspace,
+                    workspace_bytes, stream);
 }
 
 const char *fa_status_string(int status) {

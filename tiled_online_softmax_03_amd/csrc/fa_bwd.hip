@@ -1,22 +1,30 @@
 // fa_bwd.hip -- attention backward for gfx950.
 //
 // Method: page 1 "Flash Attention 原理与实现", section "Backward 的 Tiling
-// 策略" (recompute S and P block by block instead of storing them; dV = P^T dO,
-// dP = dO V^T, dQ = dS K, dK = dS^T Q; dQ and dK summed across blocks, by
-// atomics or partial sums -- section "实际实现中的注意事项", item 3), with P
-// rebuilt from the saved LSE as exp(s - LSE) (lumenova.space
+// 策略": S and P are recomputed block by block from Q, K and the saved
+// statistics instead of being stored; dV = P^T dO, dP = dO V^T, dQ = dS K,
+// dK = dS^T Q.  P is rebuilt as exp(s - LSE) (lumenova.space
 // "research-attention", section 04).  The softmax gradient is the standard
-// vector-Jacobian product dS = P * (dP - D), D_i = sum_j P_ij dP_ij, and
-// D_i = rowsum(dO_i * O_i) because O_i = sum_j P_ij V_j.
+// vector-Jacobian product dS = P * (dP - D) with D_i = sum_j P_ij dP_ij, and
+// D_i = rowsum(dO_i * O_i) because O_i = sum_j P_ij V_j.  The cross-block sums
+// of dQ and dK use the second option of page 1's section "实际实现中的注意事项"
+// (item 3): partial sums kept on chip, no atomics.
 //
-// Three launches on the caller's stream:
-//   1. bwd_pre_kernel   D = rowsum(dO * O) (fp32), zero the fp32 dQ accumulator.
-//   2. bwd_dkdv_kernel  K/V-stationary: a workgroup owns 32*NW keys of one head
-//                       (32 per wave, K and V rows kept in VGPRs), walks the
-//                       query tiles, recomputes P, accumulates dV^T and dK^T in
-//                       registers, and adds dS K into the dQ accumulator with
-//                       fp32 atomics after exchanging dS through LDS.
-//   3. bwd_dq_kernel    dQ = scale * accumulator, rounded to the output type.
+// Three launches on the caller's stream, each a stage of fa_bwd_stage:
+//   0. bwd_pre_kernel   D = rowsum(dO * O) in fp32.
+//   1. bwd_dkdv_kernel  K/V-stationary: a workgroup owns 128 keys of one head
+//                       (32 per wave, K and V rows held in VGPRs) and walks
+//                       the query tiles, recomputing S, P, dP and dS, and
+//                       accumulating dV^T += dO^T P and dK^T += Q^T dS in
+//                       registers.  Q and dO are staged row-major through LDS
+//                       (double-buffered); their transposes are read with
+//                       ds_read_b64_tr_b16.
+//   2. bwd_dq_kernel    Q-stationary: a workgroup owns 256 query rows (32 per
+//                       wave, Q and dO rows held in VGPRs) and streams K/V
+//                       tiles like the forward: S^T = K Q^T, dP^T = V dO^T,
+//                       dS^T, dQ^T += K^T dS^T.
+// dQ, dK and dV are therefore deterministic.  The price is that S and dP are
+// formed twice (7 matrix products instead of 5).
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -35,13 +43,12 @@ __device__ __forceinline__ void load8_stored(const void *base, int64_t elem, flo
     }
 }
 
-// ---------------------------------------------------------------- 1. preprocess
+// ---------------------------------------------------------------- 0. D = rowsum(dO * O)
 template <int D, int E>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const void *__restrict__ O, const void *__restrict__ dO,
-                                                      float *__restrict__ Dvec, float *__restrict__ dQacc,
-                                                      int64_t rows) {
-    constexpr int NCH = D / 8;        // lanes per row
-    constexpr int RPB = 256 / NCH;    // rows per block
+                                                      float *__restrict__ Dvec, int64_t rows) {
+    constexpr int NCH = D / 8;      // lanes per row
+    constexpr int RPB = 256 / NCH;  // rows per block
     const int tid = threadIdx.x;
     const int64_t row = (int64_t)blockIdx.x * RPB + tid / NCH;
     const int c = tid % NCH;
@@ -52,52 +59,33 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const void *__restrict__ O
         load8_float<E>(dO, row * D + c * 8, go);  // dO as the products see it
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = fmaf(o[e], go[e], acc);
-        f32x4_t *z = reinterpret_cast<f32x4_t *>(dQacc + row * D + c * 8);
-        z[0] = f32x4_t{};
-        z[1] = f32x4_t{};
     }
 #pragma unroll
     for (int off = NCH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (row < rows && c == 0) Dvec[row] = acc;
 }
 
-// ---------------------------------------------------------------- 2. dK, dV (+ dQ atomics)
-
-// Row-major 16-bit tile with rows of W elements: 16-byte chunk c of row r is
-// stored at chunk c ^ rswz<W>(r) so that 16 rows read at one chunk spread
-// over all banks.
-template <int W>
-__device__ __forceinline__ int rswz(int row) { return (row / (128 / W)) % (W / 8); }
-// Transposed 16-bit tile with rows of W elements read in 8-byte units (4
-// elements): unit u of row c is stored at unit u ^ tswz<W>(c).
-template <int W>
-__device__ __forceinline__ int tswz(int col) { return (col / (128 / W)) % (W / 4); }
-
-__device__ __forceinline__ uint32_t lo16x2(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-
-template <int D, int NW, int E, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
-    const void *__restrict__ Q, const void *__restrict__ K, const void *__restrict__ V,
-    const void *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Dvec,
-    float *__restrict__ dQacc, void *__restrict__ dK, void *__restrict__ dV, int BH, int Nq, int Nk,
-    float scale, float scale_log2, int n_kt) {
+// ---------------------------------------------------------------- 1. dK, dV
+template <int D, int E, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K,
+                                                       const void *__restrict__ V, const void *__restrict__ dO,
+                                                       const float *__restrict__ LSE, const float *__restrict__ Dvec,
+                                                       void *__restrict__ dK, void *__restrict__ dV, int BH, int Nq,
+                                                       int Nk, float scale, float scale_log2, int n_kt) {
+    constexpr int NW = 4, NT = 256;
     constexpr int BKC = 32 * NW;  // keys per workgroup
-    constexpr int BQ = 32;        // queries per step
-    constexpr int NT = NW * 64;
-    constexpr int NCH = D / 8;    // 16-byte chunks per row of Q / dO / K
+    constexpr int BQ = 64;        // query rows per step
+    constexpr int NQB = BQ / 32;  // 32-row blocks per step
+    constexpr int NCH = D / 8;    // 16-byte chunks per row
     constexpr int NKS = D / 16;   // k-steps over the head dim
     constexpr int NDB = D / 32;   // 32-row blocks of dK^T / dV^T
-    static_assert(NW % NDB == 0 || NDB % NW == 0, "wave / column-block split");
+    constexpr int CH_PER_T = BQ * NCH / NT;  // chunks of Q (and of dO) each thread stages
+    static_assert(BQ * NCH % NT == 0, "staging split");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[BQ * D];    // [q][d]
-    __shared__ __attribute__((aligned(16))) uint16_t dOs[BQ * D];   // [q][d]
-    __shared__ __attribute__((aligned(16))) uint16_t Qt[D * BQ];    // [d][q]
-    __shared__ __attribute__((aligned(16))) uint16_t dOt[D * BQ];   // [d][q]
-    __shared__ __attribute__((aligned(16))) uint16_t Kt[D * BKC];   // [d][key], whole workgroup
-    __shared__ __attribute__((aligned(16))) uint16_t dSs[BQ * BKC]; // [q][key]
-    __shared__ __attribute__((aligned(16))) float lse2[BQ];
-    __shared__ __attribute__((aligned(16))) float dvec[BQ];
+    __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * D];
+    __shared__ __attribute__((aligned(16))) uint16_t dOs[2][BQ * D];
+    __shared__ __attribute__((aligned(16))) float lse2[2][BQ];
+    __shared__ __attribute__((aligned(16))) float dvec[2][BQ];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, g = lane >> 5;
@@ -116,8 +104,51 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     const int64_t q_head = (int64_t)bh * Nq * D;
     const int64_t k_head = (int64_t)bh * Nk * D;
     const int k0 = kt * BKC;
-    const int kw = k0 + wave * 32 + l32;  // this lane's key
+    const int kw0 = k0 + wave * 32;  // first key of this wave
+    const int kw = kw0 + l32;        // this lane's key
     const int kw_ld = kw < Nk ? kw : Nk - 1;
+
+    const int n_qt = (Nq + BQ - 1) / BQ;
+    const int qt_begin = CAUSAL ? min(k0 / BQ, n_qt) : 0;  // earlier rows see none of these keys
+
+    // ---- staging of one query tile: global -> VGPR (prefetch), VGPR -> LDS
+    u32x4_t qreg[CH_PER_T], dreg[CH_PER_T];
+    float lreg = 0.f, dvreg = 0.f;
+    auto load_tile = [&](int qt) {
+        const int q0 = qt * BQ;
+#pragma unroll
+        for (int j = 0; j < CH_PER_T; ++j) {
+            const int i = tid + j * NT;
+            const int row = i / NCH, c = i % NCH;
+            const int qq = q0 + row;
+            qreg[j] = u32x4_t{0u, 0u, 0u, 0u};
+            dreg[j] = u32x4_t{0u, 0u, 0u, 0u};
+            if (qq < Nq) {
+                qreg[j] = load8_operand<E>(Q, q_head + (int64_t)qq * D + c * 8);
+                dreg[j] = load8_operand<E>(dO, q_head + (int64_t)qq * D + c * 8);
+            }
+        }
+        if (tid < BQ) {
+            const int qq = q0 + tid;
+            lreg = qq < Nq ? LSE[(int64_t)bh * Nq + qq] * kLog2e : INFINITY;  // P = 0 on padding rows
+            dvreg = qq < Nq ? Dvec[(int64_t)bh * Nq + qq] : 0.f;
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < CH_PER_T; ++j) {
+            const int i = tid + j * NT;
+            const int row = i / NCH, c = i % NCH;
+            *reinterpret_cast<u32x4_t *>(&Qs[buf][tile_off<D>(row, c * 8)]) = qreg[j];
+            *reinterpret_cast<u32x4_t *>(&dOs[buf][tile_off<D>(row, c * 8)]) = dreg[j];
+        }
+        if (tid < BQ) {
+            lse2[buf][tid] = lreg;
+            dvec[buf][tid] = dvreg;
+        }
+    };
+
+    if (qt_begin < n_qt) load_tile(qt_begin);
 
     // K and V rows of this lane's key as B operands (k = head-dim index 16*ks + 8*g + v)
     u32x4_t kf[NKS], vf[NKS];
@@ -129,156 +160,71 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
         kf[ks] = kz;
         vf[ks] = vz;
     }
-    // K^T of the whole workgroup into LDS for the dQ product: Kt[d][key]
-    for (int i = tid; i < (BKC / 4) * NCH; i += NT) {
-        const int c = i % NCH, u = i / NCH;  // keys 4u..4u+3, head dims 8c..8c+7
-        u32x4_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int key = k0 + 4 * u + k;
-            w[k] = key < Nk ? load8_operand<E>(K, k_head + (int64_t)key * D + c * 8) : u32x4_t{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int dcol = c * 8 + e;
-            const int wi = e / 2;
-            const u32x2_t val = (e & 1) ? u32x2_t{hi16x2(w[0][wi], w[1][wi]), hi16x2(w[2][wi], w[3][wi])}
-                                        : u32x2_t{lo16x2(w[0][wi], w[1][wi]), lo16x2(w[2][wi], w[3][wi])};
-            // 8-byte unit u of row dcol; rows hold BKC keys -> 16-byte chunk u/2
-            const int chunk = (u / 2) ^ rswz<BKC>(dcol);
-            *reinterpret_cast<u32x2_t *>(&Kt[dcol * BKC + chunk * 8 + (u & 1) * 4]) = val;
-        }
-    }
 
     f32x16_t dvT[NDB], dkT[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) { dvT[db] = f32x16_t{}; dkT[db] = f32x16_t{}; }
 
-    const int n_qt = (Nq + BQ - 1) / BQ;
-    const int qt_begin = CAUSAL ? min(k0 / BQ, n_qt) : 0;
-
-    // dQ work split: wave w covers column block (w % NDB) over key slice (w / NDB)
-    constexpr int WPB = NW >= NDB ? NW / NDB : 1;  // waves per column block
-    constexpr int KSL = BKC / WPB;                 // keys per slice
-    const int dq_db = wave % NDB, dq_ks = wave / NDB;
+    if (qt_begin < n_qt) store_tile(0);
+    __syncthreads();
 
     for (int qt = qt_begin; qt < n_qt; ++qt) {
-        const int q0 = qt * BQ;
-        __syncthreads();  // previous step done with every tile below
-        // ---- stage Q and dO: row-major and transposed copies
-        for (int i = tid; i < 2 * (BQ / 4) * NCH; i += NT) {
-            const int which = i / ((BQ / 4) * NCH);  // 0: Q, 1: dO
-            const int j = i % ((BQ / 4) * NCH);
-            const int c = j % NCH, u = j / NCH;      // rows 4u..4u+3, head dims 8c..8c+7
-            const void *src = which ? dO : Q;
-            uint16_t *rm = which ? dOs : Qs;
-            uint16_t *tr = which ? dOt : Qt;
-            u32x4_t w[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int qq = q0 + 4 * u + k;
-                w[k] = qq < Nq ? load8_operand<E>(src, q_head + (int64_t)qq * D + c * 8) : u32x4_t{0u, 0u, 0u, 0u};
-                const int row = 4 * u + k;
-                *reinterpret_cast<u32x4_t *>(&rm[row * D + ((c ^ rswz<D>(row)) * 8)]) = w[k];
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int dcol = c * 8 + e;
-                const int wi = e / 2;
-                const u32x2_t val = (e & 1) ? u32x2_t{hi16x2(w[0][wi], w[1][wi]), hi16x2(w[2][wi], w[3][wi])}
-                                            : u32x2_t{lo16x2(w[0][wi], w[1][wi]), lo16x2(w[2][wi], w[3][wi])};
-                *reinterpret_cast<u32x2_t *>(&tr[dcol * BQ + ((u ^ tswz<BQ>(dcol)) * 4)]) = val;
-            }
-        }
-        if (tid < BQ) {
-            const int qq = q0 + tid;
-            lse2[tid] = qq < Nq ? LSE[(int64_t)bh * Nq + qq] * kLog2e : INFINITY;  // P = 0 on padding rows
-            dvec[tid] = qq < Nq ? Dvec[(int64_t)bh * Nq + qq] : 0.f;
-        }
-        __syncthreads();
+        const int buf = (qt - qt_begin) & 1;
+        const bool more = qt + 1 < n_qt;
+        if (more) load_tile(qt + 1);  // in flight during this step's math
+        const uint16_t *qs = Qs[buf];
+        const uint16_t *ds = dOs[buf];
 
-        // ---- S = Q K^T and dP = dO V^T: lane = key, register r -> query 8*(r/4) + 4*g + r%4
-        f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int ch = ((2 * ks + g) ^ rswz<D>(l32)) * 8;
-            const u32x4_t qa = *reinterpret_cast<const u32x4_t *>(&Qs[l32 * D + ch]);
-            const u32x4_t da = *reinterpret_cast<const u32x4_t *>(&dOs[l32 * D + ch]);
-            s = mfma_in<E>(qa, kf[ks], s);
-            dp = mfma_in<E>(da, vf[ks], dp);
-        }
-        // ---- P = exp(s*scale - LSE), dS = P * (dP - D)
-        uint32_t pp[8], ds[8];
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-            const f32x4_t L4 = *reinterpret_cast<const f32x4_t *>(&lse2[8 * rq + 4 * g]);
-            const f32x4_t D4 = *reinterpret_cast<const f32x4_t *>(&dvec[8 * rq + 4 * g]);
-            float p[4], t[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * rq + i;
-                const int qq = q0 + 8 * rq + 4 * g + i;
-                float pv = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -L4[i]));
-                if (CAUSAL && kw > qq) pv = 0.f;
-                p[i] = pv;
-                t[i] = pv * (dp[r] - D4[i]);
-            }
-            pp[2 * rq] = pack_in<E>(p[0], p[1]);
-            pp[2 * rq + 1] = pack_in<E>(p[2], p[3]);
-            ds[2 * rq] = pack_in<E>(t[0], t[1]);
-            ds[2 * rq + 1] = pack_in<E>(t[2], t[3]);
-            // dS into LDS as [q][key] for the dQ product
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 8 * rq + 4 * g + i;
-                const int key = wave * 32 + l32;
-                const int chunk = (key / 8) ^ rswz<BKC>(row);
-                const uint32_t word = ds[2 * rq + i / 2];
-                dSs[row * BKC + chunk * 8 + (key % 8)] = (uint16_t)((i & 1) ? (word >> 16) : (word & 0xffffu));
-            }
-        }
-        // ---- dV^T += dO^T P and dK^T += Q^T dS (k = query; slot (g, v) -> 16h + 4g + v or 16h + 8 + 4g + v-4)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const u32x4_t bp = {pp[4 * h], pp[4 * h + 1], pp[4 * h + 2], pp[4 * h + 3]};
-            const u32x4_t bs = {ds[4 * h], ds[4 * h + 1], ds[4 * h + 2], ds[4 * h + 3]};
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int dcol = db * 32 + l32;
-                const int sw = tswz<BQ>(dcol);
-                const int o1 = dcol * BQ + (((4 * h + g) ^ sw) * 4), o2 = dcol * BQ + (((4 * h + 2 + g) ^ sw) * 4);
-                const u32x2_t a1 = *reinterpret_cast<const u32x2_t *>(&dOt[o1]);
-                const u32x2_t a2 = *reinterpret_cast<const u32x2_t *>(&dOt[o2]);
-                const u32x2_t b1 = *reinterpret_cast<const u32x2_t *>(&Qt[o1]);
-                const u32x2_t b2 = *reinterpret_cast<const u32x2_t *>(&Qt[o2]);
-                dvT[db] = mfma_in<E>(u32x4_t{a1[0], a1[1], a2[0], a2[1]}, bp, dvT[db]);
-                dkT[db] = mfma_in<E>(u32x4_t{b1[0], b1[1], b2[0], b2[1]}, bs, dkT[db]);
-            }
-        }
-        __syncthreads();  // dS of every wave in LDS
+        for (int qb = 0; qb < NQB; ++qb) {
+            const int q0 = qt * BQ + qb * 32;
+            if (CAUSAL && q0 + 31 < kw0) continue;  // every row of the block precedes this wave's keys
 
-        // ---- dQ[q][d] += dS[q][key] K[key][d] over this wave's key slice and column block
-        {
-            f32x16_t acc = f32x16_t{};
-            const int dcol = dq_db * 32 + l32;
+            // S = Q K^T and dP = dO V^T: lane = key, register r -> query q0 + 8*(r/4) + 4*g + r%4
+            f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
-            for (int kk = 0; kk < KSL / 16; ++kk) {
-                const int kc = (dq_ks * KSL) / 8 + 2 * kk + g;  // 16-byte chunk of 8 keys
-                const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&dSs[l32 * BKC + ((kc ^ rswz<BKC>(l32)) * 8)]);
-                const u32x4_t b = *reinterpret_cast<const u32x4_t *>(&Kt[dcol * BKC + ((kc ^ rswz<BKC>(dcol)) * 8)]);
-                acc = mfma_in<E>(a, b, acc);
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int off = tile_off<D>(qb * 32 + l32, 16 * ks + 8 * g);
+                s = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&qs[off]), kf[ks], s);
+                dp = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&ds[off]), vf[ks], dp);
             }
-            if (NW >= NDB || wave < NDB) {
+            // P = exp2(s*c - LSE*log2e), dS = P (dP - D)
+            uint32_t pp[8], dd[8];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qq = q0 + 8 * (r / 4) + 4 * g + (r % 4);
-                    if (qq < Nq) unsafeAtomicAdd(&dQacc[q_head + (int64_t)qq * D + dcol], acc[r]);
+            for (int rq = 0; rq < 4; ++rq) {
+                const f32x4_t L4 = *reinterpret_cast<const f32x4_t *>(&lse2[buf][qb * 32 + 8 * rq + 4 * g]);
+                const f32x4_t D4 = *reinterpret_cast<const f32x4_t *>(&dvec[buf][qb * 32 + 8 * rq + 4 * g]);
+                float p[4], t[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * rq + i;
+                    float pv = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -L4[i]));
+                    if (CAUSAL && kw > q0 + 8 * rq + 4 * g + i) pv = 0.f;
+                    p[i] = pv;
+                    t[i] = pv * (dp[r] - D4[i]);
+                }
+                pp[2 * rq] = pack_in<E>(p[0], p[1]);
+                pp[2 * rq + 1] = pack_in<E>(p[2], p[3]);
+                dd[2 * rq] = pack_in<E>(t[0], t[1]);
+                dd[2 * rq + 1] = pack_in<E>(t[2], t[3]);
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS; k-step h covers query rows 16h..16h+15 of the block
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4_t bp = {pp[4 * h], pp[4 * h + 1], pp[4 * h + 2], pp[4 * h + 3]};
+                const u32x4_t bs = {dd[4 * h], dd[4 * h + 1], dd[4 * h + 2], dd[4 * h + 3]};
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    dvT[db] = mfma_in<E>(tr_operand<D>(ds, qb * 32 + 16 * h, 32 * db, lane), bp, dvT[db]);
+                    dkT[db] = mfma_in<E>(tr_operand<D>(qs, qb * 32 + 16 * h, 32 * db, lane), bs, dkT[db]);
                 }
             }
         }
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
     }
 
-    // ---- dK = scale * dK^T^T, dV = dV^T^T: lane = key, register r -> head dim 32db + 8*(r/4) + 4*g + r%4
+    // ---- dK = scale * (dK^T)^T, dV = (dV^T)^T: lane = key, register r -> head dim 32db + 8*(r/4) + 4*g + r%4
     if (kw < Nk) {
         const int64_t row = k_head + (int64_t)kw * D;
 #pragma unroll
@@ -294,64 +240,203 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     }
 }
 
-// ---------------------------------------------------------------- 3. dQ finalise
-template <int E>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(const float *__restrict__ dQacc, void *__restrict__ dQ,
-                                                     int64_t n8, float scale) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const f32x4_t *p = reinterpret_cast<const f32x4_t *>(dQacc + i * 8);
-    const f32x4_t a = p[0], b = p[1];
-    store4<E>(dQ, i * 8, a[0] * scale, a[1] * scale, a[2] * scale, a[3] * scale);
-    store4<E>(dQ, i * 8 + 4, b[0] * scale, b[1] * scale, b[2] * scale, b[3] * scale);
+// ---------------------------------------------------------------- 2. dQ
+template <int D, int E, bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q, const void *__restrict__ K,
+                                                     const void *__restrict__ V, const void *__restrict__ dO,
+                                                     const float *__restrict__ LSE, const float *__restrict__ Dvec,
+                                                     void *__restrict__ dQ, int BH, int Nq, int Nk, float scale,
+                                                     float scale_log2, int n_qt) {
+    constexpr int NW = 8, NT = 512;
+    constexpr int BR = 32 * NW;   // query rows per workgroup
+    constexpr int BC = 32;        // keys per tile
+    constexpr int NCH = D / 8;
+    constexpr int NKS = D / 16;
+    constexpr int NDB = D / 32;
+    constexpr int CH = BC * NCH;  // 16-byte chunks per K (and V) tile
+    constexpr int CH_PER_T = (CH + NT - 1) / NT;
+
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BC * D];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, g = lane >> 5;
+
+    int bh, qt;
+    if constexpr (CAUSAL) {
+        const int L = blockIdx.x;  // longest rows first
+        qt = n_qt - 1 - L / BH;
+        bh = L % BH;
+    } else {
+        const int L = xcd_remap(blockIdx.x, gridDim.x);
+        bh = L / n_qt;
+        qt = L % n_qt;
+    }
+    const int64_t q_head = (int64_t)bh * Nq * D;
+    const int64_t k_head = (int64_t)bh * Nk * D;
+    const int q_wave0 = qt * BR + wave * 32;
+    const int q = q_wave0 + l32;  // this lane's query row
+    const int q_ld = q < Nq ? q : Nq - 1;
+
+    int k_end = Nk;
+    if constexpr (CAUSAL) k_end = min(Nk, min(qt * BR + BR, Nq));
+    const int n_kt = (k_end + BC - 1) / BC;
+
+    u32x4_t kreg[CH_PER_T], vreg[CH_PER_T];
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < CH_PER_T; ++j) {
+            const int i = tid + j * NT;
+            const int row = i / NCH, c = i % NCH;
+            kreg[j] = u32x4_t{0u, 0u, 0u, 0u};
+            vreg[j] = u32x4_t{0u, 0u, 0u, 0u};
+            if (i < CH && k0 + row < Nk) {
+                kreg[j] = load8_operand<E>(K, k_head + (int64_t)(k0 + row) * D + c * 8);
+                vreg[j] = load8_operand<E>(V, k_head + (int64_t)(k0 + row) * D + c * 8);
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < CH_PER_T; ++j) {
+            const int i = tid + j * NT;
+            const int row = i / NCH, c = i % NCH;
+            if (i < CH) {
+                *reinterpret_cast<u32x4_t *>(&Ks[buf][tile_off<D>(row, c * 8)]) = kreg[j];
+                *reinterpret_cast<u32x4_t *>(&Vs[buf][tile_off<D>(row, c * 8)]) = vreg[j];
+            }
+        }
+    };
+
+    load_tile(0);
+
+    // Q^T and dO^T fragments (B operands, k = head-dim index 16*ks + 8*g + v) and row statistics
+    u32x4_t qf[NKS], df[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        qf[ks] = load8_operand<E>(Q, q_head + (int64_t)q_ld * D + 16 * ks + 8 * g);
+        df[ks] = load8_operand<E>(dO, q_head + (int64_t)q_ld * D + 16 * ks + 8 * g);
+    }
+    const float lse2 = LSE[(int64_t)bh * Nq + q_ld] * kLog2e;
+    const float dv = Dvec[(int64_t)bh * Nq + q_ld];
+
+    f32x16_t dqT[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dqT[db] = f32x16_t{};
+
+    store_tile(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int k0 = kt * BC;
+        const int buf = kt & 1;
+        const bool more = kt + 1 < n_kt;
+        if (more) load_tile(k0 + BC);
+
+        if (!CAUSAL || k0 <= q_wave0 + 31) {
+            // S^T = K Q^T and dP^T = V dO^T: lane = query, register r -> key k0 + 8*(r/4) + 4*g + r%4
+            f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int off = tile_off<D>(l32, 16 * ks + 8 * g);
+                s = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&Ks[buf][off]), qf[ks], s);
+                dp = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&Vs[buf][off]), df[ks], dp);
+            }
+            const bool ragged = k0 + BC > Nk;
+            const bool diag = CAUSAL && (k0 + BC - 1 > q_wave0);
+            uint32_t dd[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float t[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int r = 2 * i + e;
+                    float pv = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -lse2));
+                    if (ragged || diag) {
+                        const int key = k0 + 8 * (r / 4) + 4 * g + (r % 4);
+                        if (key >= Nk || (CAUSAL && key > q)) pv = 0.f;
+                    }
+                    t[e] = pv * (dp[r] - dv);
+                }
+                dd[i] = pack_in<E>(t[0], t[1]);
+            }
+            // dQ^T += K^T dS^T; k-step h covers keys k0 + 16h .. k0 + 16h + 15
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4_t b = {dd[4 * h], dd[4 * h + 1], dd[4 * h + 2], dd[4 * h + 3]};
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    dqT[db] = mfma_in<E>(tr_operand<D>(Ks[buf], 16 * h, 32 * db, lane), b, dqT[db]);
+            }
+        }
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- dQ = scale * (dQ^T)^T: lane = query, register r -> head dim 32db + 8*(r/4) + 4*g + r%4
+    if (q < Nq) {
+        const int64_t row = q_head + (int64_t)q * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq)
+                store4<E>(dQ, row + db * 32 + 8 * rq + 4 * g, dqT[db][4 * rq] * scale, dqT[db][4 * rq + 1] * scale,
+                          dqT[db][4 * rq + 2] * scale, dqT[db][4 * rq + 3] * scale);
+    }
 }
 
 template <int D, int E, bool CAUSAL>
-static hipError_t launch_bwd_t(const BwdArgs &a) {
-    constexpr int NW = 4, BKC = 32 * NW;
+static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
     hipStream_t st = (hipStream_t)a.stream;
     const int BH = a.B * a.H;
     const int64_t rows = (int64_t)BH * a.Nq;
-    {
+    const float sl2 = a.scale * kLog2e;
+    if (stage < 0 || stage == 0) {
         constexpr int RPB = 256 / (D / 8);
         hipLaunchKernelGGL((bwd_pre_kernel<D, E>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, a.O,
-                           a.dO, a.Dvec, a.dQacc, rows);
+                           a.dO, a.Dvec, rows);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    {
-        const int n_kt = (a.Nk + BKC - 1) / BKC;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, E, CAUSAL>), dim3(BH * n_kt), dim3(NW * 64), 0, st, a.Q, a.K, a.V,
-                           a.dO, a.LSE, a.Dvec, a.dQacc, a.dK, a.dV, BH, a.Nq, a.Nk, a.scale, a.scale * kLog2e, n_kt);
+    if (stage < 0 || stage == 1) {
+        const int n_kt = (a.Nk + 127) / 128;
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, E, CAUSAL>), dim3(BH * n_kt), dim3(256), 0, st, a.Q, a.K, a.V, a.dO,
+                           a.LSE, a.Dvec, a.dK, a.dV, BH, a.Nq, a.Nk, a.scale, sl2, n_kt);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    {
-        const int64_t n8 = rows * D / 8;
-        hipLaunchKernelGGL((bwd_dq_kernel<E>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, a.dQacc, a.dQ, n8,
-                           a.scale);
-        return hipGetLastError();
+    if (stage < 0 || stage == 2) {
+        const int n_qt = (a.Nq + 255) / 256;
+        hipLaunchKernelGGL((bwd_dq_kernel<D, E, CAUSAL>), dim3(BH * n_qt), dim3(512), 0, st, a.Q, a.K, a.V, a.dO,
+                           a.LSE, a.Dvec, a.dQ, BH, a.Nq, a.Nk, a.scale, sl2, n_qt);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
+    return hipSuccess;
 }
 
 template <int D, int E>
-static hipError_t launch_bwd_c(const BwdArgs &a) {
-    return a.causal ? launch_bwd_t<D, E, true>(a) : launch_bwd_t<D, E, false>(a);
+static hipError_t launch_bwd_c(const BwdArgs &a, int stage) {
+    return a.causal ? launch_bwd_t<D, E, true>(a, stage) : launch_bwd_t<D, E, false>(a, stage);
 }
 
 template <int D>
-static hipError_t launch_bwd_d(const BwdArgs &a) {
+static hipError_t launch_bwd_d(const BwdArgs &a, int stage) {
     switch (a.dtype) {
-        case ELT_BF16: return launch_bwd_c<D, ELT_BF16>(a);
-        case ELT_F16: return launch_bwd_c<D, ELT_F16>(a);
-        default: return launch_bwd_c<D, ELT_F32>(a);
+        case ELT_BF16: return launch_bwd_c<D, ELT_BF16>(a, stage);
+        case ELT_F16: return launch_bwd_c<D, ELT_F16>(a, stage);
+        default: return launch_bwd_c<D, ELT_F32>(a, stage);
     }
 }
 
-hipError_t launch_bwd(const BwdArgs &a) { return a.d == 64 ? launch_bwd_d<64>(a) : launch_bwd_d<128>(a); }
+hipError_t launch_bwd(const BwdArgs &a, int stage) {
+    return a.d == 64 ? launch_bwd_d<64>(a, stage) : launch_bwd_d<128>(a, stage);
+}
 
 const char *describe_bwd() {
-    return "bwd_pre_kernel -> bwd_dkdv_kernel<D, waves=4 (128 keys), query step 32, fp32 dQ atomics> -> bwd_dq_kernel";
+    return "bwd_pre_kernel (D=rowsum(dO*O)) -> bwd_dkdv_kernel<D, 4 waves x 32 keys, 64-row query steps, "
+           "double-buffered Q/dO, transposed LDS reads> -> bwd_dq_kernel<D, 8 waves x 32 rows, 32-key tiles>; "
+           "no atomics";
 }
 
 }  // namespace fa

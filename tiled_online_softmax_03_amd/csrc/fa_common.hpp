@@ -115,6 +115,24 @@ __device__ __forceinline__ void load8_float(const void *base, int64_t elem, floa
     }
 }
 
+// Four consecutive elements of an E-typed row as floats (fp32 rounded to
+// bf16 first, as everywhere else).
+template <int E>
+__device__ __forceinline__ void load4_float(const void *base, int64_t elem, float out[4]) {
+    if constexpr (E == ELT_F32) {
+        const f32x4_t a = *reinterpret_cast<const f32x4_t *>(static_cast<const float *>(base) + elem);
+        const uint32_t w0 = pack_bf16(a[0], a[1]), w1 = pack_bf16(a[2], a[3]);
+        out[0] = bf16_lo(w0); out[1] = bf16_hi(w0); out[2] = bf16_lo(w1); out[3] = bf16_hi(w1);
+    } else {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(base) + elem);
+        if constexpr (E == ELT_BF16) {
+            out[0] = bf16_lo(w[0]); out[1] = bf16_hi(w[0]); out[2] = bf16_lo(w[1]); out[3] = bf16_hi(w[1]);
+        } else {
+            out[0] = f16_lo(w[0]); out[1] = f16_hi(w[0]); out[2] = f16_lo(w[1]); out[3] = f16_hi(w[1]);
+        }
+    }
+}
+
 // Store four consecutive floats to an E-typed row (RNE for 16-bit types).
 template <int E>
 __device__ __forceinline__ void store4(void *base, int64_t elem, float a, float b, float c, float d) {
@@ -125,6 +143,46 @@ __device__ __forceinline__ void store4(void *base, int64_t elem, float a, float 
     } else {
         *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(base) + elem) = u32x2_t{pack_f16(a, b), pack_f16(c, d)};
     }
+}
+
+// Row-major 16-bit LDS tile with rows of W elements: 16-byte chunk c of row r
+// is stored at chunk c ^ swz<W>(r).  Eight consecutive rows read at one chunk
+// (ds_read_b128) and the 4-row x 32-byte blocks of a transposed read
+// (ds_read_b64_tr_b16) both land on distinct banks.
+template <int W>
+__device__ __forceinline__ int swz(int row) {
+    int s = ((row & 3) << 1) | ((row >> 2) & 1);
+    if constexpr (W / 8 >= 16) s |= (row & 8);
+    return s;
+}
+
+// Element offset of (row, col) in such a tile; col must be a multiple of 4.
+template <int W>
+__device__ __forceinline__ int tile_off(int row, int col) {
+    return row * W + (((col >> 3) ^ swz<W>(row)) << 3) + (col & 7);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
+// halfword (i % 4) of the 8-byte chunks addressed by lanes i/4, i/4 + 4,
+// i/4 + 8 and i/4 + 12 of its group, in that order.
+__device__ __forceinline__ u32x2_t ds_read_tr16(const uint16_t *p) {
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)p);
+    return __builtin_bit_cast(u32x2_t, v);
+}
+
+// MFMA A operand holding T^T, read transposed from a row-major swizzled LDS
+// tile T[k][m] (rows of W elements): lane l gets m = m0 + l%32 and the k
+// slots v = 0..3 -> row r0 + 4g + v, v = 4..7 -> row r0 + 8 + 4g + (v-4),
+// g = l/32 -- the row order of a 32x32 accumulator's registers 8h..8h+7.
+template <int W>
+__device__ __forceinline__ u32x4_t tr_operand(const uint16_t *T, int r0, int m0, int lane) {
+    const int j = lane & 15, g = lane >> 5;
+    const int col = m0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+    const int row = r0 + 4 * g + (j >> 2);
+    const u32x2_t a = ds_read_tr16(T + tile_off<W>(row, col));
+    const u32x2_t b = ds_read_tr16(T + tile_off<W>(row + 8, col));
+    return u32x4_t{a[0], a[1], b[0], b[1]};
 }
 
 // Map a hardware workgroup index to a logical one so that consecutive

@@ -38,6 +38,14 @@ __device__ __forceinline__ int kswz(int row) { return (row / (128 / D)) % (D / 8
 template <int BC>
 __device__ __forceinline__ int vswz(int col) { return (col / (128 / BC)) % (BC / 4); }
 
+// Rescale threshold (log2 units): the running maximum used for the
+// exponentials is only moved when a new score exceeds it by more than this,
+// so p = exp2(s*c - m_used) stays below 2^8 (far inside fp16 range) and the
+// accumulator is rescaled only on the rare tiles that raise the maximum.
+// O = u / l and LSE = m_used + log2 l hold for any m_used, so this changes no
+// result beyond rounding.
+constexpr float kRescaleThreshold = 8.f;
+
 template <int D, int BC, int NW, int E, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
                                                       const void *__restrict__ V, void *__restrict__ O,
@@ -49,10 +57,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q
     constexpr int NKB = BC / 32;   // 32-key blocks per tile
     constexpr int NDB = D / 32;    // 32-column blocks of O
     constexpr int NKS = D / 16;    // k-steps of the QK^T product
-    constexpr int NUNIT = BC / 4;  // 8-byte units per V^T row
+    constexpr int NUNIT = BC / 4;  // 8-byte units (4 keys) per V^T row
+    // K staging: 16-byte chunks per thread; V staging: (4 keys x 4 columns) blocks per thread
+    constexpr int KCH_PER_T = (BC * NCH + NT - 1) / NT;
+    constexpr int VBLK = NUNIT * (D / 4);
+    constexpr int VBLK_PER_T = (VBLK + NT - 1) / NT;
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * D];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * BC];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * BC];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, g = lane >> 5;
@@ -75,6 +87,61 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q
     const int q = q_wave0 + l32;  // this lane's query row
     const int q_ld = q < Nq ? q : Nq - 1;
 
+    int k_end = Nk;
+    if constexpr (CAUSAL) k_end = min(Nk, min(qt * BR + BR, Nq));  // keys <= last query of the workgroup
+    const int n_kt = (k_end + BC - 1) / BC;
+
+    // ---- register prefetch of one K/V tile (global -> VGPR), then VGPR -> LDS
+    u32x4_t kreg[KCH_PER_T];
+    float vreg[VBLK_PER_T][4][4];  // [block][key][column]
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < KCH_PER_T; ++j) {
+            const int i = tid + j * NT;
+            const int row = i / NCH, c = i % NCH;
+            kreg[j] = u32x4_t{0u, 0u, 0u, 0u};
+            if (i < BC * NCH && k0 + row < Nk) kreg[j] = load8_operand<E>(K, k_head + (int64_t)(k0 + row) * D + c * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < VBLK_PER_T; ++j) {
+            const int i = tid + j * NT;
+            const int c4 = i % (D / 4), u = i / (D / 4);  // keys 4u..4u+3, columns 4c4..4c4+3
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int key = k0 + 4 * u + k;
+                if (i < VBLK && key < Nk) {
+                    load4_float<E>(V, k_head + (int64_t)key * D + 4 * c4, vreg[j][k]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vreg[j][k][e] = 0.f;
+                }
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < KCH_PER_T; ++j) {
+            const int i = tid + j * NT;
+            const int row = i / NCH, c = i % NCH;
+            if (i < BC * NCH) *reinterpret_cast<u32x4_t *>(&Ks[buf][row * D + ((c ^ kswz<D>(row)) * 8)]) = kreg[j];
+        }
+#pragma unroll
+        for (int j = 0; j < VBLK_PER_T; ++j) {
+            const int i = tid + j * NT;
+            const int c4 = i % (D / 4), u = i / (D / 4);
+            if (i < VBLK) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int col = 4 * c4 + e;
+                    *reinterpret_cast<u32x2_t *>(&Vt[buf][col * BC + ((u ^ vswz<BC>(col)) * 4)]) =
+                        u32x2_t{pack_f16(vreg[j][0][e], vreg[j][1][e]), pack_f16(vreg[j][2][e], vreg[j][3][e])};
+                }
+            }
+        }
+    };
+
+    load_tile(0);
+
     // Q^T fragments: B operand of S^T = K Q^T, k = head-dim index 16*ks + 8*g + v
     u32x4_t qf[NKS];
 #pragma unroll
@@ -83,124 +150,100 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q
     f32x16_t o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x16_t{};
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_used = -INFINITY, l_run = 0.f;
+    const f16x2_t ones = {(_Float16)1.f, (_Float16)1.f};
 
-    int k_end = Nk;
-    if constexpr (CAUSAL) {
-        const int q_last = min(qt * BR + BR, Nq);  // one past the last query of the workgroup
-        k_end = min(Nk, q_last);
-    }
-    const int n_kt = (k_end + BC - 1) / BC;
+    store_tile(0);
+    __syncthreads();
 
     for (int kt = 0; kt < n_kt; ++kt) {
         const int k0 = kt * BC;
-        __syncthreads();  // previous tile fully consumed
-        // ---- stage K (row-major, swizzled) and V^T (fp16, swizzled)
+        const int buf = kt & 1;
+        const bool more = kt + 1 < n_kt;
+        if (more) load_tile(k0 + BC);  // in flight during this tile's math
+
+        if (!CAUSAL || k0 <= q_wave0 + 31) {  // else the tile lies above the diagonal for every row of this wave
+            // ---- S^T = K Q^T : lane = query, register r -> key 8*(r/4) + 4*g + r%4 of each 32-key block
+            f32x16_t s[NKB];
 #pragma unroll
-        for (int i = tid; i < BC * NCH; i += NT) {
-            const int row = i / NCH, c = i % NCH;
-            u32x4_t w = {0u, 0u, 0u, 0u};
-            if (k0 + row < Nk) w = load8_operand<E>(K, k_head + (int64_t)(k0 + row) * D + c * 8);
-            *reinterpret_cast<u32x4_t *>(&Ks[row * D + ((c ^ kswz<D>(row)) * 8)]) = w;
-        }
+            for (int kb = 0; kb < NKB; ++kb) {
+                s[kb] = f32x16_t{};
+                const int row = kb * 32 + l32;
 #pragma unroll
-        for (int i = tid; i < NUNIT * NCH; i += NT) {
-            const int c = i % NCH, u = i / NCH;  // keys 4u..4u+3, columns 8c..8c+7
-            float v[4][8];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int key = k0 + 4 * u + k;
-                if (key < Nk) {
-                    load8_float<E>(V, k_head + (int64_t)key * D + c * 8, v[k]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[k][e] = 0.f;
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const u32x4_t a =
+                        *reinterpret_cast<const u32x4_t *>(&Ks[buf][row * D + (((2 * ks + g) ^ kswz<D>(row)) * 8)]);
+                    s[kb] = mfma_in<E>(a, qf[ks], s[kb]);
                 }
             }
+
+            const bool ragged = k0 + BC > Nk;
+            const bool diag = CAUSAL && (k0 + BC - 1 > q_wave0);
+            if (ragged || diag) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int col = c * 8 + e;
-                *reinterpret_cast<u32x2_t *>(&Vt[col * BC + ((u ^ vswz<BC>(col)) * 4)]) =
-                    u32x2_t{pack_f16(v[0][e], v[1][e]), pack_f16(v[2][e], v[3][e])};
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + kb * 32 + 8 * (r / 4) + 4 * g + (r % 4);
+                        if (key >= Nk || (CAUSAL && key > q)) s[kb][r] = -INFINITY;
+                    }
             }
-        }
-        __syncthreads();
 
-        if (CAUSAL && k0 > q_wave0 + 31) continue;  // tile lies above the diagonal for every row of this wave
-
-        // ---- S^T = K Q^T : lane = query, register r -> key 8*(r/4) + 4*g + r%4 of each 32-key block
-        f32x16_t s[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            s[kb] = f32x16_t{};
-            const int row = kb * 32 + l32;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&Ks[row * D + (((2 * ks + g) ^ kswz<D>(row)) * 8)]);
-                s[kb] = mfma_in<E>(a, qf[ks], s[kb]);
-            }
-        }
-
-        const bool ragged = k0 + BC > Nk;
-        const bool diag = CAUSAL && (k0 + BC - 1 > q_wave0);
-        if (ragged || diag) {
+            // ---- tile max; move the reference maximum only when it grows past the threshold
+            float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kb * 32 + 8 * (r / 4) + 4 * g + (r % 4);
-                    if (key >= Nk || (CAUSAL && key > q)) s[kb][r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = half_max(mx) * scale_log2;  // scale > 0, so max commutes with it
+            if (__ballot(mx > m_used + kRescaleThreshold) != 0) {  // wave-uniform branch
+                const float m_new = fmaxf(m_used, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
+                m_used = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            }
+
+            // ---- P = exp2(s*c - m_used) rounded to fp16; l += sum of the rounded values
+            uint32_t pk[NKB][8];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i], scale_log2, -m_used));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i + 1], scale_log2, -m_used));
+                    pk[kb][i] = pack_f16(p0, p1);
+                    l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk[kb][i]), ones, l_run, false);
                 }
-        }
 
-        // ---- running max / rescale / exponentials / running sum
-        float mx = -INFINITY;
+            // ---- O^T += V^T P^T (fp16 matrix core).  k-step kst covers keys
+            // 16*kst .. 16*kst+15; slot (g, v) holds key 16*kst + 4g + v (v < 4)
+            // or 16*kst + 8 + 4g + (v-4), matching the S^T register order.
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+            for (int kst = 0; kst < BC / 16; ++kst) {
+                const int kb = kst / 2, h = kst % 2;
+                const u32x4_t b = {pk[kb][4 * h], pk[kb][4 * h + 1], pk[kb][4 * h + 2], pk[kb][4 * h + 3]};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = half_max(mx);
-        const float m_new = fmaxf(m_run, mx * scale_log2);  // scale > 0, so max commutes with it
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-
-        uint32_t pk[NKB][8];
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i], scale_log2, -m_new));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i + 1], scale_log2, -m_new));
-                lsum += p0 + p1;
-                pk[kb][i] = pack_f16(p0, p1);
-            }
-        l_run += lsum;
-
-        // ---- O^T += V^T P^T (fp16 matrix core).  k-step kst covers keys
-        // 16*kst .. 16*kst+15; slot (g, v) holds key 16*kst + 4g + v (v < 4)
-        // or 16*kst + 8 + 4g + (v-4), matching the S^T register order.
-#pragma unroll
-        for (int kst = 0; kst < BC / 16; ++kst) {
-            const int kb = kst / 2, h = kst % 2;
-            const u32x4_t b = {pk[kb][4 * h], pk[kb][4 * h + 1], pk[kb][4 * h + 2], pk[kb][4 * h + 3]};
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int col = db * 32 + l32;
-                const int sw = vswz<BC>(col);
-                const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(&Vt[col * BC + (((4 * kst + g) ^ sw) * 4)]);
-                const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(&Vt[col * BC + (((4 * kst + 2 + g) ^ sw) * 4)]);
-                o[db] = mfma_f16(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, b, o[db]);
+                for (int db = 0; db < NDB; ++db) {
+                    const int col = db * 32 + l32;
+                    const int sw = vswz<BC>(col);
+                    const u32x2_t lo =
+                        *reinterpret_cast<const u32x2_t *>(&Vt[buf][col * BC + (((4 * kst + g) ^ sw) * 4)]);
+                    const u32x2_t hi =
+                        *reinterpret_cast<const u32x2_t *>(&Vt[buf][col * BC + (((4 * kst + 2 + g) ^ sw) * 4)]);
+                    o[db] = mfma_f16(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, b, o[db]);
+                }
             }
         }
+
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
     }
 
-    // ---- epilogue: O = u / l, LSE = (m2 + log2 l) * ln 2
+    // ---- epilogue: O = u / l, LSE = (m_used + log2 l) * ln 2
     const float l_tot = half_sum(l_run);
     const float inv = 1.f / l_tot;
     if (q < Nq) {
@@ -211,13 +254,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q
             for (int rq = 0; rq < 4; ++rq)
                 store4<E>(O, orow + db * 32 + 8 * rq + 4 * g, o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv,
                           o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
-        if (g == 0) LSE[(int64_t)bh * Nq + q] = (m_run + __builtin_log2f(l_tot)) * kLn2;
+        if (g == 0) LSE[(int64_t)bh * Nq + q] = (m_used + __builtin_log2f(l_tot)) * kLn2;
     }
 }
 
 template <int D, int E, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs &a) {
-    constexpr int BC = 64, NW = 4, BR = 32 * NW;
+    constexpr int BC = 64, NW = 8, BR = 32 * NW;
     const int n_qt = (a.Nq + BR - 1) / BR;
     const int BH = a.B * a.H;
     const dim3 grid(BH * n_qt), block(NW * 64);
@@ -242,6 +285,9 @@ static hipError_t launch_fwd_d(const FwdArgs &a) {
 
 hipError_t launch_fwd(const FwdArgs &a) { return a.d == 64 ? launch_fwd_d<64>(a) : launch_fwd_d<128>(a); }
 
-const char *describe_fwd() { return "fwd_kernel<D, BC=64, waves=4 (128 query rows), S^T=KQ^T bf16/f16 MFMA 32x32x16, PV fp16 MFMA>"; }
+const char *describe_fwd() {
+    return "fwd_kernel<D, BC=64, waves=8 (256 query rows, 32 per wave), double-buffered K/V^T in LDS, "
+           "S^T=KQ^T bf16/f16 MFMA 32x32x16, PV fp16 MFMA, lazy rescale>";
+}
 
 }  // namespace fa

@@ -24,13 +24,14 @@ struct BwdArgs {
     int B, H, Nq, Nk, d;
     float scale;
     int causal, dtype;
-    float *Dvec;   // [B*H*Nq] workspace: rowsum(dO * O)
-    float *dQacc;  // [B*H*Nq*d] workspace: unscaled fp32 dQ accumulator
+    float *Dvec;  // [B*H*Nq] workspace: rowsum(dO * O)
     void *stream;
 };
 
 hipError_t launch_fwd(const FwdArgs &a);
-hipError_t launch_bwd(const BwdArgs &a);
+constexpr int kBwdStages = 3;
+// stage < 0 runs every stage in order.
+hipError_t launch_bwd(const BwdArgs &a, int stage);
 const char *describe_fwd();
 const char *describe_bwd();
 
