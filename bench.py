@@ -11,7 +11,7 @@ times, a roofline entry for the dominant kernel and a CPU baseline (the fp64
 oracle timed on a bounded sample of the same workload on this host).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
-                    [--no-cpu-baseline] [--cpu-heads 8]
+                    [--no-cpu-baseline] [--cpu-heads 48] [--copy-probe-mib 0]
 """
 from __future__ import annotations
 
@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--workload", default="train_b8h32n4096d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=48, help="heads in the oracle's timed sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size reference "
+                         "for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -132,6 +135,15 @@ def main():
         roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": units,
                 "avg_launch_ms": kern_ms[dom]}
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -24,7 +24,8 @@ import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfa.so")
+# LIBFA_PATH selects another build of the same library (e.g. to compare builds).
+LIB_PATH = os.environ.get("LIBFA_PATH") or os.path.join(_HERE, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_BF16, FA_F16, FA_F32 = 0, 1, 2

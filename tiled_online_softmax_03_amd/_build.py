@@ -18,6 +18,12 @@ LIB = os.path.join(HERE, "libfa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+# Per-source extra flags.  The K/V-stationary backward kernel runs one wave per
+# SIMD; left to its heuristics the backend then gives every matrix product
+# AGPR accumulators, and the softmax-gradient math (VALU, which cannot read
+# AGPRs) pays a copy of S and dP into VGPRs on every block.  VGPR-form
+# products avoid that.
+EXTRA = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -29,25 +35,25 @@ DEVICE = ["-x", "hip", "--offload-arch=" + ARCH, "-munsafe-fp-atomics",
 def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD_DIR, src + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE, "-c", path, "-o", obj]
+    cmd = [HIPCC, *COMMON, *DEVICE, *EXTRA.get(src, []), "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
-def build(jobs: int = 4) -> str:
-    """Compile every HIP source and link libfa.so; returns its path."""
+def build(jobs: int = 4, out: str = LIB) -> str:
+    """Compile every HIP source and link libfa.so (or `out`); returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -13,7 +13,7 @@
 // Three launches on the caller's stream, each a stage of fa_bwd_stage:
 //   0. bwd_pre_kernel   D = rowsum(dO * O) in fp32.
 //   1. bwd_dkdv_kernel  K/V-stationary: a workgroup owns 128 keys of one head
-//                       (32 per wave, K and V rows held in VGPRs) and walks
+//                       (32 per wave; K rows in VGPRs, V rows in LDS) and walks
 //                       the query tiles, recomputing S, P, dP and dS, and
 //                       accumulating dV^T += dO^T P and dK^T += Q^T dS in
 //                       registers.  Q and dO are staged row-major through LDS
@@ -79,11 +79,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const void *__restrict__ 
     constexpr int NCH = D / 8;    // 16-byte chunks per row
     constexpr int NKS = D / 16;   // k-steps over the head dim
     constexpr int NDB = D / 32;   // 32-row blocks of dK^T / dV^T
-    constexpr int CH_PER_T = BQ * NCH / NT;  // chunks of Q (and of dO) each thread stages
+    constexpr bool DMA = E != ELT_F32;  // 16-bit Q / dO go global -> LDS directly
+    constexpr int CH_PER_T = DMA ? 1 : BQ * NCH / NT;  // register staging (fp32 -> bf16)
     static_assert(BQ * NCH % NT == 0, "staging split");
 
     __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * D];
     __shared__ __attribute__((aligned(16))) uint16_t dOs[2][BQ * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[BKC * D];  // this workgroup's V rows
     __shared__ __attribute__((aligned(16))) float lse2[2][BQ];
     __shared__ __attribute__((aligned(16))) float dvec[2][BQ];
 
@@ -111,21 +113,48 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const void *__restrict__ 
     const int n_qt = (Nq + BQ - 1) / BQ;
     const int qt_begin = CAUSAL ? min(k0 / BQ, n_qt) : 0;  // earlier rows see none of these keys
 
-    // ---- staging of one query tile: global -> VGPR (prefetch), VGPR -> LDS
+    // K rows of this lane's key as B operands (k = head-dim index 16*ks + 8*g + v), held
+    // in VGPRs; the workgroup's V rows go to LDS once and are read from there, which keeps
+    // the kernel under 256 VGPRs so every matrix product uses VGPR accumulators.  Both
+    // are loaded before any tile prefetch so waiting for them never waits on a prefetch.
+    u32x4_t kf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        u32x4_t kz = load8_operand<E>(K, k_head + (int64_t)kw_ld * D + 16 * ks + 8 * g);
+        if (kw >= Nk) kz = u32x4_t{0u, 0u, 0u, 0u};
+        kf[ks] = kz;
+    }
+#pragma unroll
+    for (int j = 0; j < BKC * NCH / NT; ++j) {
+        const int i = tid + j * NT;
+        const int row = i / NCH, c = i % NCH;
+        u32x4_t w = {0u, 0u, 0u, 0u};
+        if (k0 + row < Nk) w = load8_operand<E>(V, k_head + (int64_t)(k0 + row) * D + c * 8);
+        *reinterpret_cast<u32x4_t *>(&Vs[tile_off<D>(row, c * 8)]) = w;
+    }
+
+    // ---- staging of one query tile
+    const void *Qh = static_cast<const char *>(Q) + q_head * (E == ELT_F32 ? 4 : 2);
+    const void *dOh = static_cast<const char *>(dO) + q_head * (E == ELT_F32 ? 4 : 2);
     u32x4_t qreg[CH_PER_T], dreg[CH_PER_T];
     float lreg = 0.f, dvreg = 0.f;
-    auto load_tile = [&](int qt) {
+    auto load_tile = [&](int qt, int buf) {
         const int q0 = qt * BQ;
+        if constexpr (DMA) {
+            dma_tile<D, BQ, NW>(Qh, q0, Nq, Qs[buf], wave, lane);
+            dma_tile<D, BQ, NW>(dOh, q0, Nq, dOs[buf], wave, lane);
+        } else {
 #pragma unroll
-        for (int j = 0; j < CH_PER_T; ++j) {
-            const int i = tid + j * NT;
-            const int row = i / NCH, c = i % NCH;
-            const int qq = q0 + row;
-            qreg[j] = u32x4_t{0u, 0u, 0u, 0u};
-            dreg[j] = u32x4_t{0u, 0u, 0u, 0u};
-            if (qq < Nq) {
-                qreg[j] = load8_operand<E>(Q, q_head + (int64_t)qq * D + c * 8);
-                dreg[j] = load8_operand<E>(dO, q_head + (int64_t)qq * D + c * 8);
+            for (int j = 0; j < CH_PER_T; ++j) {
+                const int i = tid + j * NT;
+                const int row = i / NCH, c = i % NCH;
+                const int qq = q0 + row;
+                qreg[j] = u32x4_t{0u, 0u, 0u, 0u};
+                dreg[j] = u32x4_t{0u, 0u, 0u, 0u};
+                if (qq < Nq) {
+                    qreg[j] = load8_operand<E>(Q, q_head + (int64_t)qq * D + c * 8);
+                    dreg[j] = load8_operand<E>(dO, q_head + (int64_t)qq * D + c * 8);
+                }
             }
         }
         if (tid < BQ) {
@@ -135,12 +164,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const void *__restrict__ 
         }
     };
     auto store_tile = [&](int buf) {
+        if constexpr (!DMA) {
 #pragma unroll
-        for (int j = 0; j < CH_PER_T; ++j) {
-            const int i = tid + j * NT;
-            const int row = i / NCH, c = i % NCH;
-            *reinterpret_cast<u32x4_t *>(&Qs[buf][tile_off<D>(row, c * 8)]) = qreg[j];
-            *reinterpret_cast<u32x4_t *>(&dOs[buf][tile_off<D>(row, c * 8)]) = dreg[j];
+            for (int j = 0; j < CH_PER_T; ++j) {
+                const int i = tid + j * NT;
+                const int row = i / NCH, c = i % NCH;
+                *reinterpret_cast<u32x4_t *>(&Qs[buf][tile_off<D>(row, c * 8)]) = qreg[j];
+                *reinterpret_cast<u32x4_t *>(&dOs[buf][tile_off<D>(row, c * 8)]) = dreg[j];
+            }
         }
         if (tid < BQ) {
             lse2[buf][tid] = lreg;
@@ -148,30 +179,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const void *__restrict__ 
         }
     };
 
-    if (qt_begin < n_qt) load_tile(qt_begin);
-
-    // K and V rows of this lane's key as B operands (k = head-dim index 16*ks + 8*g + v)
-    u32x4_t kf[NKS], vf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        u32x4_t kz = load8_operand<E>(K, k_head + (int64_t)kw_ld * D + 16 * ks + 8 * g);
-        u32x4_t vz = load8_operand<E>(V, k_head + (int64_t)kw_ld * D + 16 * ks + 8 * g);
-        if (kw >= Nk) { kz = u32x4_t{0u, 0u, 0u, 0u}; vz = kz; }
-        kf[ks] = kz;
-        vf[ks] = vz;
-    }
-
     f32x16_t dvT[NDB], dkT[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) { dvT[db] = f32x16_t{}; dkT[db] = f32x16_t{}; }
 
-    if (qt_begin < n_qt) store_tile(0);
+    if (qt_begin < n_qt) {
+        load_tile(qt_begin, 0);
+        store_tile(0);
+    }
+    wait_vmem();
     __syncthreads();
 
     for (int qt = qt_begin; qt < n_qt; ++qt) {
         const int buf = (qt - qt_begin) & 1;
         const bool more = qt + 1 < n_qt;
-        if (more) load_tile(qt + 1);  // in flight during this step's math
+        if (more) load_tile(qt + 1, buf ^ 1);  // in flight during this step's math
         const uint16_t *qs = Qs[buf];
         const uint16_t *ds = dOs[buf];
 
@@ -185,8 +207,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const void *__restrict__ 
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const int off = tile_off<D>(qb * 32 + l32, 16 * ks + 8 * g);
+                const u32x4_t vb = *reinterpret_cast<const u32x4_t *>(&Vs[tile_off<D>(wave * 32 + l32, 16 * ks + 8 * g)]);
                 s = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&qs[off]), kf[ks], s);
-                dp = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&ds[off]), vf[ks], dp);
+                dp = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&ds[off]), vb, dp);
             }
             // P = exp2(s*c - LSE*log2e), dS = P (dP - D)
             uint32_t pp[8], dd[8];
@@ -219,8 +242,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const void *__restrict__ 
                     dkT[db] = mfma_in<E>(tr_operand<D>(qs, qb * 32 + 16 * h, 32 * db, lane), bs, dkT[db]);
                 }
             }
+            // one 32-row block in flight at a time keeps S, dP, P and dS of a single
+            // block live, which lets the dK/dV accumulators stay in registers
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (more) store_tile(buf ^ 1);
+        wait_vmem();
         __syncthreads();
     }
 
@@ -241,7 +268,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const void *__restrict__ 
 }
 
 // ---------------------------------------------------------------- 2. dQ
-template <int D, int E, bool CAUSAL>
+template <int D, int BC, int E, bool CAUSAL>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q, const void *__restrict__ K,
                                                      const void *__restrict__ V, const void *__restrict__ dO,
                                                      const float *__restrict__ LSE, const float *__restrict__ Dvec,
@@ -249,12 +276,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
                                                      float scale_log2, int n_qt) {
     constexpr int NW = 8, NT = 512;
     constexpr int BR = 32 * NW;   // query rows per workgroup
-    constexpr int BC = 32;        // keys per tile
+    constexpr int NKB = BC / 32;  // 32-key blocks per tile
     constexpr int NCH = D / 8;
     constexpr int NKS = D / 16;
     constexpr int NDB = D / 32;
-    constexpr int CH = BC * NCH;  // 16-byte chunks per K (and V) tile
-    constexpr int CH_PER_T = (CH + NT - 1) / NT;
+    constexpr bool DMA = E != ELT_F32;  // 16-bit K / V go global -> LDS directly
+    constexpr int CH = BC * NCH;        // 16-byte chunks per K (and V) tile
+    constexpr int CH_PER_T = DMA ? 1 : (CH + NT - 1) / NT;
 
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * D];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BC * D];
@@ -282,35 +310,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
     if constexpr (CAUSAL) k_end = min(Nk, min(qt * BR + BR, Nq));
     const int n_kt = (k_end + BC - 1) / BC;
 
-    u32x4_t kreg[CH_PER_T], vreg[CH_PER_T];
-    auto load_tile = [&](int k0) {
-#pragma unroll
-        for (int j = 0; j < CH_PER_T; ++j) {
-            const int i = tid + j * NT;
-            const int row = i / NCH, c = i % NCH;
-            kreg[j] = u32x4_t{0u, 0u, 0u, 0u};
-            vreg[j] = u32x4_t{0u, 0u, 0u, 0u};
-            if (i < CH && k0 + row < Nk) {
-                kreg[j] = load8_operand<E>(K, k_head + (int64_t)(k0 + row) * D + c * 8);
-                vreg[j] = load8_operand<E>(V, k_head + (int64_t)(k0 + row) * D + c * 8);
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < CH_PER_T; ++j) {
-            const int i = tid + j * NT;
-            const int row = i / NCH, c = i % NCH;
-            if (i < CH) {
-                *reinterpret_cast<u32x4_t *>(&Ks[buf][tile_off<D>(row, c * 8)]) = kreg[j];
-                *reinterpret_cast<u32x4_t *>(&Vs[buf][tile_off<D>(row, c * 8)]) = vreg[j];
-            }
-        }
-    };
-
-    load_tile(0);
-
-    // Q^T and dO^T fragments (B operands, k = head-dim index 16*ks + 8*g + v) and row statistics
+    // Q^T and dO^T fragments (B operands, k = head-dim index 16*ks + 8*g + v) and the
+    // row statistics, loaded before any tile prefetch.
     u32x4_t qf[NKS], df[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -320,56 +321,101 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
     const float lse2 = LSE[(int64_t)bh * Nq + q_ld] * kLog2e;
     const float dv = Dvec[(int64_t)bh * Nq + q_ld];
 
+    const void *Kh = static_cast<const char *>(K) + k_head * (E == ELT_F32 ? 4 : 2);
+    const void *Vh = static_cast<const char *>(V) + k_head * (E == ELT_F32 ? 4 : 2);
+    u32x4_t kreg[CH_PER_T], vreg[CH_PER_T];
+    auto load_tile = [&](int k0, int buf) {
+        if constexpr (DMA) {
+            dma_tile<D, BC, NW>(Kh, k0, Nk, Ks[buf], wave, lane);
+            dma_tile<D, BC, NW>(Vh, k0, Nk, Vs[buf], wave, lane);
+        } else {
+#pragma unroll
+            for (int j = 0; j < CH_PER_T; ++j) {
+                const int i = tid + j * NT;
+                const int row = i / NCH, c = i % NCH;
+                kreg[j] = u32x4_t{0u, 0u, 0u, 0u};
+                vreg[j] = u32x4_t{0u, 0u, 0u, 0u};
+                if (i < CH && k0 + row < Nk) {
+                    kreg[j] = load8_operand<E>(K, k_head + (int64_t)(k0 + row) * D + c * 8);
+                    vreg[j] = load8_operand<E>(V, k_head + (int64_t)(k0 + row) * D + c * 8);
+                }
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        if constexpr (!DMA) {
+#pragma unroll
+            for (int j = 0; j < CH_PER_T; ++j) {
+                const int i = tid + j * NT;
+                const int row = i / NCH, c = i % NCH;
+                if (i < CH) {
+                    *reinterpret_cast<u32x4_t *>(&Ks[buf][tile_off<D>(row, c * 8)]) = kreg[j];
+                    *reinterpret_cast<u32x4_t *>(&Vs[buf][tile_off<D>(row, c * 8)]) = vreg[j];
+                }
+            }
+        }
+    };
+
     f32x16_t dqT[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dqT[db] = f32x16_t{};
 
+    load_tile(0, 0);
     store_tile(0);
+    wait_vmem();
     __syncthreads();
 
     for (int kt = 0; kt < n_kt; ++kt) {
         const int k0 = kt * BC;
         const int buf = kt & 1;
         const bool more = kt + 1 < n_kt;
-        if (more) load_tile(k0 + BC);
+        if (more) load_tile(k0 + BC, buf ^ 1);
 
         if (!CAUSAL || k0 <= q_wave0 + 31) {
-            // S^T = K Q^T and dP^T = V dO^T: lane = query, register r -> key k0 + 8*(r/4) + 4*g + r%4
-            f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+            // S^T = K Q^T and dP^T = V dO^T: lane = query, register r -> key k0 + 32kb + 8*(r/4) + 4*g + r%4
+            f32x16_t s[NKB], dp[NKB];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const int off = tile_off<D>(l32, 16 * ks + 8 * g);
-                s = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&Ks[buf][off]), qf[ks], s);
-                dp = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&Vs[buf][off]), df[ks], dp);
-            }
+            for (int kb = 0; kb < NKB; ++kb) { s[kb] = f32x16_t{}; dp[kb] = f32x16_t{}; }
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const int off = tile_off<D>(kb * 32 + l32, 16 * ks + 8 * g);
+                    s[kb] = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&Ks[buf][off]), qf[ks], s[kb]);
+                    dp[kb] = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&Vs[buf][off]), df[ks], dp[kb]);
+                }
             const bool ragged = k0 + BC > Nk;
             const bool diag = CAUSAL && (k0 + BC - 1 > q_wave0);
-            uint32_t dd[8];
+            uint32_t dd[NKB][8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float t[2];
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int r = 2 * i + e;
-                    float pv = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -lse2));
-                    if (ragged || diag) {
-                        const int key = k0 + 8 * (r / 4) + 4 * g + (r % 4);
-                        if (key >= Nk || (CAUSAL && key > q)) pv = 0.f;
+                for (int i = 0; i < 8; ++i) {
+                    float t[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int r = 2 * i + e;
+                        float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -lse2));
+                        if (ragged || diag) {
+                            const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * g + (r % 4);
+                            if (key >= Nk || (CAUSAL && key > q)) pv = 0.f;
+                        }
+                        t[e] = pv * (dp[kb][r] - dv);
                     }
-                    t[e] = pv * (dp[r] - dv);
+                    dd[kb][i] = pack_in<E>(t[0], t[1]);
                 }
-                dd[i] = pack_in<E>(t[0], t[1]);
-            }
-            // dQ^T += K^T dS^T; k-step h covers keys k0 + 16h .. k0 + 16h + 15
+            // dQ^T += K^T dS^T; k-step kst covers keys k0 + 16kst .. k0 + 16kst + 15
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const u32x4_t b = {dd[4 * h], dd[4 * h + 1], dd[4 * h + 2], dd[4 * h + 3]};
+            for (int kst = 0; kst < BC / 16; ++kst) {
+                const int kb = kst / 2, h = kst % 2;
+                const u32x4_t b = {dd[kb][4 * h], dd[kb][4 * h + 1], dd[kb][4 * h + 2], dd[kb][4 * h + 3]};
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
-                    dqT[db] = mfma_in<E>(tr_operand<D>(Ks[buf], 16 * h, 32 * db, lane), b, dqT[db]);
+                    dqT[db] = mfma_in<E>(tr_operand<D>(Ks[buf], 16 * kst, 32 * db, lane), b, dqT[db]);
             }
         }
         if (more) store_tile(buf ^ 1);
+        wait_vmem();
         __syncthreads();
     }
 
@@ -384,6 +430,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
                           dqT[db][4 * rq + 2] * scale, dqT[db][4 * rq + 3] * scale);
     }
 }
+
+constexpr int kDqKeys = 64;  // keys per tile of the dQ pass
 
 template <int D, int E, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
@@ -407,7 +455,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
     }
     if (stage < 0 || stage == 2) {
         const int n_qt = (a.Nq + 255) / 256;
-        hipLaunchKernelGGL((bwd_dq_kernel<D, E, CAUSAL>), dim3(BH * n_qt), dim3(512), 0, st, a.Q, a.K, a.V, a.dO,
+        hipLaunchKernelGGL((bwd_dq_kernel<D, (E == ELT_F32 ? 32 : kDqKeys), E, CAUSAL>), dim3(BH * n_qt), dim3(512), 0, st, a.Q, a.K, a.V, a.dO,
                            a.LSE, a.Dvec, a.dQ, BH, a.Nq, a.Nk, a.scale, sl2, n_qt);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -435,7 +483,7 @@ hipError_t launch_bwd(const BwdArgs &a, int stage) {
 
 const char *describe_bwd() {
     return "bwd_pre_kernel (D=rowsum(dO*O)) -> bwd_dkdv_kernel<D, 4 waves x 32 keys, 64-row query steps, "
-           "double-buffered Q/dO, transposed LDS reads> -> bwd_dq_kernel<D, 8 waves x 32 rows, 32-key tiles>; "
+           "double-buffered Q/dO, transposed LDS reads> -> bwd_dq_kernel<D, 8 waves x 32 rows, 64-key tiles>; "
            "no atomics";
 }
 

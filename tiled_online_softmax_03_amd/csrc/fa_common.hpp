@@ -185,6 +185,35 @@ __device__ __forceinline__ u32x4_t tr_operand(const uint16_t *T, int r0, int m0,
     return u32x4_t{a[0], a[1], b[0], b[1]};
 }
 
+// Wait until every vector-memory operation of this wave has completed,
+// including global -> LDS copies (which the compiler does not track).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Copy rows [row0, row0 + R) of a row-major 16-bit global matrix with rows of
+// W elements into an LDS tile in tile_off<W> layout, using
+// global_load_lds_dwordx4: one wave instruction fills 1 KiB of LDS, lane l
+// the 16 bytes at 16*l, so each lane fetches the global chunk that the
+// swizzle places there.  Rows at or past `nrows` re-read row nrows-1 (finite
+// data; callers give such rows zero weight).  Blocks are spread over the
+// NWAVES waves of the workgroup.  Completion: wait_vmem() then a barrier.
+template <int W, int R, int NWAVES>
+__device__ __forceinline__ void dma_tile(const void *g, int row0, int nrows, uint16_t *lds, int wave, int lane) {
+    constexpr int RPB = 512 / W;  // rows per 1 KiB block
+    constexpr int NBLK = R / RPB;
+    static_assert(R % RPB == 0, "tile rows must fill whole 1 KiB blocks");
+    const int r_in = lane / (W / 8), p = lane % (W / 8);
+#pragma unroll
+    for (int b = wave; b < NBLK; b += NWAVES) {
+        const int r = b * RPB + r_in;
+        const int c = p ^ swz<W>(r);
+        int grow = row0 + r;
+        grow = grow < nrows ? grow : nrows - 1;
+        const uint16_t *src = static_cast<const uint16_t *>(g) + (int64_t)grow * W + c * 8;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (__attribute__((address_space(3))) void *)(lds + b * 512), 16, 0, 0);
+    }
+}
+
 // Map a hardware workgroup index to a logical one so that consecutive
 // logical indices land on the same XCD.  Workgroups are handed to the eight
 // XCDs round-robin; this is a bijection on [0, n).

@@ -7,12 +7,14 @@
 // p = exp(s - m'), l' = alpha l + sum p, u' = alpha u + sum p v, one division
 // at the end) and LSE = m + ln l saved for the backward (same page, section 04).
 //
-// MI355X mapping (one workgroup = NW waves = 32*NW query rows of one head):
+// MI355X mapping (one workgroup = NW waves = 32*NW query rows of one head,
+// two waves per SIMD):
 //  * Each wave keeps its 32 query rows in VGPRs for the whole key loop.
-//  * K and V tiles of BC keys are staged through LDS, shared by all waves.
-//    K stays row-major (XOR-swizzled 16-byte chunks); V is written
-//    transposed and converted to fp16 while staging, so the P*V product reads
-//    it as an MFMA A operand with two 8-byte LDS reads.
+//  * K and V tiles of BC keys are double-buffered in LDS, shared by all
+//    waves; the next tile is fetched while the current one is in use.  K
+//    stays row-major (XOR-swizzled 16-byte chunks) and is copied global ->
+//    LDS directly; V is converted to fp16 and written transposed, so the
+//    P*V product reads each operand with one 16-byte LDS read.
 //  * Scores are formed transposed, S^T = K Q^T, so each lane owns one query
 //    row: the row max and row sum are in-lane reductions plus one
 //    permlane32 swap, and the rescale of the accumulator is one multiply per
@@ -27,16 +29,14 @@
 
 namespace fa {
 
-// K tile in LDS: [BC][D] 16-bit, 16-byte chunk c of row r lives at chunk
-// c ^ kswz(r); chosen so 16 consecutive rows read at one chunk hit distinct
-// banks.
-template <int D>
-__device__ __forceinline__ int kswz(int row) { return (row / (128 / D)) % (D / 8); }
-
-// V^T tile in LDS: [D][BC] fp16, 8-byte unit u (4 keys) of row c lives at
-// unit u ^ vswz(c).
+// V^T tile in LDS: [D][BC] fp16.  Each row holds, per 16-key group kst, two
+// 16-byte chunks: chunk 2*kst + g carries keys 16kst + 4g + 0..3 and
+// 16kst + 8 + 4g + 0..3, exactly the eight k-slots lane group g feeds to the
+// PV matrix product, so one ds_read_b128 fetches a whole operand.  Chunks are
+// XOR-swizzled per row so that eight consecutive rows read at one chunk hit
+// distinct banks.
 template <int BC>
-__device__ __forceinline__ int vswz(int col) { return (col / (128 / BC)) % (BC / 4); }
+__device__ __forceinline__ int vtswz(int col) { return (col + col / (BC / 8)) % (BC / 8); }
 
 // Rescale threshold (log2 units): the running maximum used for the
 // exponentials is only moved when a new score exceeds it by more than this,
@@ -57,10 +57,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q
     constexpr int NKB = BC / 32;   // 32-key blocks per tile
     constexpr int NDB = D / 32;    // 32-column blocks of O
     constexpr int NKS = D / 16;    // k-steps of the QK^T product
-    constexpr int NUNIT = BC / 4;  // 8-byte units (4 keys) per V^T row
-    // K staging: 16-byte chunks per thread; V staging: (4 keys x 4 columns) blocks per thread
+    constexpr bool DMA = E != ELT_F32;  // 16-bit K goes global -> LDS directly
+    // K register staging (fp32 inputs only): 16-byte chunks per thread
     constexpr int KCH_PER_T = (BC * NCH + NT - 1) / NT;
-    constexpr int VBLK = NUNIT * (D / 4);
+    // V staging: blocks of 4 keys x 4 columns per thread
+    constexpr int VBLK = (BC / 4) * (D / 4);
     constexpr int VBLK_PER_T = (VBLK + NT - 1) / NT;
 
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * D];
@@ -91,16 +92,29 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q
     if constexpr (CAUSAL) k_end = min(Nk, min(qt * BR + BR, Nq));  // keys <= last query of the workgroup
     const int n_kt = (k_end + BC - 1) / BC;
 
-    // ---- register prefetch of one K/V tile (global -> VGPR), then VGPR -> LDS
-    u32x4_t kreg[KCH_PER_T];
-    float vreg[VBLK_PER_T][4][4];  // [block][key][column]
-    auto load_tile = [&](int k0) {
+    // Q^T fragments: B operand of S^T = K Q^T, k = head-dim index 16*ks + 8*g + v.
+    // Loaded before any tile prefetch so waiting for them never waits on a prefetch.
+    u32x4_t qf[NKS];
 #pragma unroll
-        for (int j = 0; j < KCH_PER_T; ++j) {
-            const int i = tid + j * NT;
-            const int row = i / NCH, c = i % NCH;
-            kreg[j] = u32x4_t{0u, 0u, 0u, 0u};
-            if (i < BC * NCH && k0 + row < Nk) kreg[j] = load8_operand<E>(K, k_head + (int64_t)(k0 + row) * D + c * 8);
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = load8_operand<E>(Q, q_head + (int64_t)q_ld * D + 16 * ks + 8 * g);
+
+    // ---- tile staging.  K: DMA (16-bit) or registers (fp32 -> bf16).  V: registers,
+    // converted to fp16 and written transposed.
+    const void *Kh = static_cast<const char *>(K) + k_head * (E == ELT_F32 ? 4 : 2);
+    u32x4_t kreg[DMA ? 1 : KCH_PER_T];
+    uint32_t vraw[VBLK_PER_T][4][2];  // [block][key][2 words of 4 columns] in the input type
+    float vf32[E == ELT_F32 ? VBLK_PER_T : 1][4][4];
+    auto load_tile = [&](int k0, int buf) {
+        if constexpr (DMA) {
+            dma_tile<D, BC, NW>(Kh, k0, Nk, Ks[buf], wave, lane);
+        } else {
+#pragma unroll
+            for (int j = 0; j < KCH_PER_T; ++j) {
+                const int i = tid + j * NT;
+                const int row = i / NCH, c = i % NCH;
+                kreg[j] = u32x4_t{0u, 0u, 0u, 0u};
+                if (i < BC * NCH && k0 + row < Nk) kreg[j] = load8_operand<E>(K, k_head + (int64_t)(k0 + row) * D + c * 8);
+            }
         }
 #pragma unroll
         for (int j = 0; j < VBLK_PER_T; ++j) {
@@ -109,43 +123,62 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int key = k0 + 4 * u + k;
-                if (i < VBLK && key < Nk) {
-                    load4_float<E>(V, k_head + (int64_t)key * D + 4 * c4, vreg[j][k]);
-                } else {
+                const bool ok = i < VBLK && key < Nk;
+                if constexpr (E == ELT_F32) {
+                    f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+                    if (ok) x = *reinterpret_cast<const f32x4_t *>(static_cast<const float *>(V) + k_head + (int64_t)key * D + 4 * c4);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) vreg[j][k][e] = 0.f;
+                    for (int e = 0; e < 4; ++e) vf32[j][k][e] = x[e];
+                } else {
+                    u32x2_t w = {0u, 0u};
+                    if (ok) w = *reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(V) + k_head + (int64_t)key * D + 4 * c4);
+                    vraw[j][k][0] = w[0];
+                    vraw[j][k][1] = w[1];
                 }
             }
         }
     };
     auto store_tile = [&](int buf) {
+        if constexpr (!DMA) {
 #pragma unroll
-        for (int j = 0; j < KCH_PER_T; ++j) {
-            const int i = tid + j * NT;
-            const int row = i / NCH, c = i % NCH;
-            if (i < BC * NCH) *reinterpret_cast<u32x4_t *>(&Ks[buf][row * D + ((c ^ kswz<D>(row)) * 8)]) = kreg[j];
+            for (int j = 0; j < KCH_PER_T; ++j) {
+                const int i = tid + j * NT;
+                const int row = i / NCH, c = i % NCH;
+                if (i < BC * NCH) *reinterpret_cast<u32x4_t *>(&Ks[buf][tile_off<D>(row, c * 8)]) = kreg[j];
+            }
         }
 #pragma unroll
         for (int j = 0; j < VBLK_PER_T; ++j) {
             const int i = tid + j * NT;
             const int c4 = i % (D / 4), u = i / (D / 4);
             if (i < VBLK) {
+                float v[4][4];  // [key][column]
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if constexpr (E == ELT_F32) {
+                        // the operand precision of fp32 data is bf16
+                        const uint32_t w0 = pack_bf16(vf32[j][k][0], vf32[j][k][1]);
+                        const uint32_t w1 = pack_bf16(vf32[j][k][2], vf32[j][k][3]);
+                        v[k][0] = bf16_lo(w0); v[k][1] = bf16_hi(w0); v[k][2] = bf16_lo(w1); v[k][3] = bf16_hi(w1);
+                    } else if constexpr (E == ELT_BF16) {
+                        v[k][0] = bf16_lo(vraw[j][k][0]); v[k][1] = bf16_hi(vraw[j][k][0]);
+                        v[k][2] = bf16_lo(vraw[j][k][1]); v[k][3] = bf16_hi(vraw[j][k][1]);
+                    } else {
+                        v[k][0] = f16_lo(vraw[j][k][0]); v[k][1] = f16_hi(vraw[j][k][0]);
+                        v[k][2] = f16_lo(vraw[j][k][1]); v[k][3] = f16_hi(vraw[j][k][1]);
+                    }
+                }
+                const int kst = u / 4, qd = u % 4;  // 16-key group, key quad inside it
+                const int chunk = 2 * kst + (qd & 1), half = qd >> 1;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int col = 4 * c4 + e;
-                    *reinterpret_cast<u32x2_t *>(&Vt[buf][col * BC + ((u ^ vswz<BC>(col)) * 4)]) =
-                        u32x2_t{pack_f16(vreg[j][0][e], vreg[j][1][e]), pack_f16(vreg[j][2][e], vreg[j][3][e])};
+                    *reinterpret_cast<u32x2_t *>(&Vt[buf][col * BC + ((chunk ^ vtswz<BC>(col)) * 8) + half * 4]) =
+                        u32x2_t{pack_f16(v[0][e], v[1][e]), pack_f16(v[2][e], v[3][e])};
                 }
             }
         }
     };
-
-    load_tile(0);
-
-    // Q^T fragments: B operand of S^T = K Q^T, k = head-dim index 16*ks + 8*g + v
-    u32x4_t qf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = load8_operand<E>(Q, q_head + (int64_t)q_ld * D + 16 * ks + 8 * g);
 
     f32x16_t o[NDB];
 #pragma unroll
@@ -153,29 +186,29 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q
     float m_used = -INFINITY, l_run = 0.f;
     const f16x2_t ones = {(_Float16)1.f, (_Float16)1.f};
 
+    load_tile(0, 0);
     store_tile(0);
+    wait_vmem();
     __syncthreads();
 
     for (int kt = 0; kt < n_kt; ++kt) {
         const int k0 = kt * BC;
         const int buf = kt & 1;
         const bool more = kt + 1 < n_kt;
-        if (more) load_tile(k0 + BC);  // in flight during this tile's math
+        if (more) load_tile(k0 + BC, buf ^ 1);  // in flight during this tile's math
 
         if (!CAUSAL || k0 <= q_wave0 + 31) {  // else the tile lies above the diagonal for every row of this wave
             // ---- S^T = K Q^T : lane = query, register r -> key 8*(r/4) + 4*g + r%4 of each 32-key block
             f32x16_t s[NKB];
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                s[kb] = f32x16_t{};
-                const int row = kb * 32 + l32;
+            for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16_t{};
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const u32x4_t a =
-                        *reinterpret_cast<const u32x4_t *>(&Ks[buf][row * D + (((2 * ks + g) ^ kswz<D>(row)) * 8)]);
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {  // independent accumulation chains back to back
+                    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&Ks[buf][tile_off<D>(kb * 32 + l32, 16 * ks + 8 * g)]);
                     s[kb] = mfma_in<E>(a, qf[ks], s[kb]);
                 }
-            }
 
             const bool ragged = k0 + BC > Nk;
             const bool diag = CAUSAL && (k0 + BC - 1 > q_wave0);
@@ -229,17 +262,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const int col = db * 32 + l32;
-                    const int sw = vswz<BC>(col);
-                    const u32x2_t lo =
-                        *reinterpret_cast<const u32x2_t *>(&Vt[buf][col * BC + (((4 * kst + g) ^ sw) * 4)]);
-                    const u32x2_t hi =
-                        *reinterpret_cast<const u32x2_t *>(&Vt[buf][col * BC + (((4 * kst + 2 + g) ^ sw) * 4)]);
-                    o[db] = mfma_f16(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, b, o[db]);
+                    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(
+                        &Vt[buf][col * BC + (((2 * kst + g) ^ vtswz<BC>(col)) * 8)]);
+                    o[db] = mfma_f16(a, b, o[db]);
                 }
             }
         }
 
         if (more) store_tile(buf ^ 1);
+        wait_vmem();
         __syncthreads();
     }
 
