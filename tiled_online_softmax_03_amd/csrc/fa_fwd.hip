@@ -24,6 +24,8 @@
 //    1e-3 relative-L2 budget; V converts from bf16 to fp16 exactly.
 //  * Softmax runs in base 2 with the scale folded into one FMA:
 //    p = exp2(s * scale*log2e - m2), m2 the running max in log2 units.
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -47,7 +49,8 @@ __device__ __forceinline__ int vtswz(int col) { return (col + col / (BC / 8)) % 
 constexpr float kRescaleThreshold = 8.f;
 
 template <int D, int BC, int NW, int E, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
                                                       const void *__restrict__ V, void *__restrict__ O,
                                                       float *__restrict__ LSE, int BH, int Nq, int Nk,
                                                       float scale_log2, int n_qt) {
@@ -116,27 +119,34 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q
                 if (i < BC * NCH && k0 + row < Nk) kreg[j] = load8_operand<E>(K, k_head + (int64_t)(k0 + row) * D + c * 8);
             }
         }
+        // Interior tiles (every key exists) take an unguarded path: a uniform branch
+        // instead of one exec-masked load per key.
+        auto load_v = [&](auto guarded_c) {
+            constexpr bool guarded = decltype(guarded_c)::value;
 #pragma unroll
-        for (int j = 0; j < VBLK_PER_T; ++j) {
-            const int i = tid + j * NT;
-            const int c4 = i % (D / 4), u = i / (D / 4);  // keys 4u..4u+3, columns 4c4..4c4+3
+            for (int j = 0; j < VBLK_PER_T; ++j) {
+                const int i = tid + j * NT;
+                const int c4 = i % (D / 4), u = i / (D / 4);  // keys 4u..4u+3, columns 4c4..4c4+3
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int key = k0 + 4 * u + k;
-                const bool ok = i < VBLK && key < Nk;
-                if constexpr (E == ELT_F32) {
-                    f32x4_t x = {0.f, 0.f, 0.f, 0.f};
-                    if (ok) x = *reinterpret_cast<const f32x4_t *>(static_cast<const float *>(V) + k_head + (int64_t)key * D + 4 * c4);
+                for (int k = 0; k < 4; ++k) {
+                    const int key = k0 + 4 * u + k;
+                    const bool ok = (VBLK % NT == 0 || i < VBLK) && (!guarded || key < Nk);
+                    if constexpr (E == ELT_F32) {
+                        f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+                        if (ok) x = *reinterpret_cast<const f32x4_t *>(static_cast<const float *>(V) + k_head + (int64_t)key * D + 4 * c4);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) vf32[j][k][e] = x[e];
-                } else {
-                    u32x2_t w = {0u, 0u};
-                    if (ok) w = *reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(V) + k_head + (int64_t)key * D + 4 * c4);
-                    vraw[j][k][0] = w[0];
-                    vraw[j][k][1] = w[1];
+                        for (int e = 0; e < 4; ++e) vf32[j][k][e] = x[e];
+                    } else {
+                        u32x2_t w = {0u, 0u};
+                        if (ok) w = *reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(V) + k_head + (int64_t)key * D + 4 * c4);
+                        vraw[j][k][0] = w[0];
+                        vraw[j][k][1] = w[1];
+                    }
                 }
             }
-        }
+        };
+        if (k0 + BC <= Nk) load_v(std::false_type{});
+        else load_v(std::true_type{});
     };
     auto store_tile = [&](int buf) {
         if constexpr (!DMA) {
@@ -191,12 +201,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q
     wait_vmem();
     __syncthreads();
 
-    for (int kt = 0; kt < n_kt; ++kt) {
+    // One key tile; BUF is the LDS buffer it reads (compile-time, so every LDS
+    // address is a fixed offset from a per-lane base).
+    auto step = [&](int kt, auto buf_c) {
+        constexpr int buf = decltype(buf_c)::value;
         const int k0 = kt * BC;
-        const int buf = kt & 1;
         const bool more = kt + 1 < n_kt;
         if (more) load_tile(k0 + BC, buf ^ 1);  // in flight during this tile's math
-
         if (!CAUSAL || k0 <= q_wave0 + 31) {  // else the tile lies above the diagonal for every row of this wave
             // ---- S^T = K Q^T : lane = query, register r -> key 8*(r/4) + 4*g + r%4 of each 32-key block
             f32x16_t s[NKB];
@@ -272,6 +283,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q
         if (more) store_tile(buf ^ 1);
         wait_vmem();
         __syncthreads();
+    };
+    for (int kt = 0; kt < n_kt; kt += 2) {
+        step(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < n_kt) step(kt + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- epilogue: O = u / l, LSE = (m_used + log2 l) * ln 2
@@ -289,9 +304,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const void *__restrict__ Q
     }
 }
 
+// Launch shape: waves per workgroup (32 query rows each) and keys per tile.
+#ifndef FA_FWD_WAVES
+#define FA_FWD_WAVES 8
+#endif
+#ifndef FA_FWD_KEYS
+#define FA_FWD_KEYS 64
+#endif
+
 template <int D, int E, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs &a) {
-    constexpr int BC = 64, NW = 8, BR = 32 * NW;
+    constexpr int BC = FA_FWD_KEYS, NW = FA_FWD_WAVES, BR = 32 * NW;
     const int n_qt = (a.Nq + BR - 1) / BR;
     const int BH = a.B * a.H;
     const dim3 grid(BH * n_qt), block(NW * 64);
