@@ -18,12 +18,8 @@ LIB = os.path.join(HERE, "libfa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
-# Per-source extra flags.  The K/V-stationary backward kernel runs one wave per
-# SIMD; left to its heuristics the backend then gives every matrix product
-# AGPR accumulators, and the softmax-gradient math (VALU, which cannot read
-# AGPRs) pays a copy of S and dP into VGPRs on every block.  VGPR-form
-# products avoid that.
-EXTRA = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extra flags (none needed by default; variants for measurements set them).
+EXTRA = {}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

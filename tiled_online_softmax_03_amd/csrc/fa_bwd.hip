@@ -12,8 +12,9 @@
 //
 // Three launches on the caller's stream, each a stage of fa_bwd_stage:
 //   0. bwd_pre_kernel   D = rowsum(dO * O) in fp32.
-//   1. bwd_dkdv_kernel  K/V-stationary: a workgroup owns 128 keys of one head
-//                       (32 per wave; K rows in VGPRs, V rows in LDS) and walks
+//   1. bwd_dkdv_kernel  K/V-stationary: a workgroup owns 256 keys of one head
+//                       (8 waves, two per SIMD, 32 keys each; K rows in VGPRs,
+//                       V rows in LDS) and walks
 //                       the query tiles, recomputing S, P, dP and dS, and
 //                       accumulating dV^T += dO^T P and dK^T += Q^T dS in
 //                       registers.  Q and dO are staged row-major through LDS
@@ -25,6 +26,8 @@
 //                       dS^T, dQ^T += K^T dS^T.
 // dQ, dK and dV are therefore deterministic.  The price is that S and dP are
 // formed twice (7 matrix products instead of 5).
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -66,13 +69,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const void *__restrict__ O
 }
 
 // ---------------------------------------------------------------- 1. dK, dV
-template <int D, int E, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K,
-                                                       const void *__restrict__ V, const void *__restrict__ dO,
-                                                       const float *__restrict__ LSE, const float *__restrict__ Dvec,
-                                                       void *__restrict__ dK, void *__restrict__ dV, int BH, int Nq,
-                                                       int Nk, float scale, float scale_log2, int n_kt) {
-    constexpr int NW = 4, NT = 256;
+template <int D, int NW, int E, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
+void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, const void *__restrict__ V,
+                     const void *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Dvec,
+                     void *__restrict__ dK, void *__restrict__ dV, int BH, int Nq, int Nk, float scale,
+                     float scale_log2, int n_kt) {
+    constexpr int NT = NW * 64;
     constexpr int BKC = 32 * NW;  // keys per workgroup
     constexpr int BQ = 64;        // query rows per step
     constexpr int NQB = BQ / 32;  // 32-row blocks per step
@@ -190,8 +193,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const void *__restrict__ 
     wait_vmem();
     __syncthreads();
 
-    for (int qt = qt_begin; qt < n_qt; ++qt) {
-        const int buf = (qt - qt_begin) & 1;
+    // One query tile; BUF (compile-time) is the LDS buffer it reads, so every LDS
+    // address is a fixed offset from a per-lane base.
+    auto step = [&](int qt, auto buf_c) {
+        const int buf = buf_c;
         const bool more = qt + 1 < n_qt;
         if (more) load_tile(qt + 1, buf ^ 1);  // in flight during this step's math
         const uint16_t *qs = Qs[buf];
@@ -249,7 +254,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const void *__restrict__ 
         if (more) store_tile(buf ^ 1);
         wait_vmem();
         __syncthreads();
+    };
+#if FA_DKDV_UNROLL
+    for (int qt = qt_begin; qt < n_qt; qt += 2) {
+        step(qt, std::integral_constant<int, 0>{});
+        if (qt + 1 < n_qt) step(qt + 1, std::integral_constant<int, 1>{});
     }
+#else
+    for (int qt = qt_begin; qt < n_qt; ++qt) step(qt, (qt - qt_begin) & 1);
+#endif
 
     // ---- dK = scale * (dK^T)^T, dV = (dV^T)^T: lane = key, register r -> head dim 32db + 8*(r/4) + 4*g + r%4
     if (kw < Nk) {
@@ -365,9 +378,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
     wait_vmem();
     __syncthreads();
 
-    for (int kt = 0; kt < n_kt; ++kt) {
+    auto step = [&](int kt, auto buf_c) {
+        constexpr int buf = decltype(buf_c)::value;
         const int k0 = kt * BC;
-        const int buf = kt & 1;
         const bool more = kt + 1 < n_kt;
         if (more) load_tile(k0 + BC, buf ^ 1);
 
@@ -417,6 +430,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
         if (more) store_tile(buf ^ 1);
         wait_vmem();
         __syncthreads();
+    };
+    for (int kt = 0; kt < n_kt; kt += 2) {
+        step(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < n_kt) step(kt + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- dQ = scale * (dQ^T)^T: lane = query, register r -> head dim 32db + 8*(r/4) + 4*g + r%4
@@ -432,6 +449,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
 }
 
 constexpr int kDqKeys = 64;  // keys per tile of the dQ pass
+#ifndef FA_DKDV_UNROLL
+#define FA_DKDV_UNROLL 1      // unroll the dK/dV query loop by two (immediate LDS offsets, more VGPRs)
+#endif
+#ifndef FA_DKDV_WAVES
+#define FA_DKDV_WAVES 8       // waves (32 keys each) per workgroup of the dK/dV pass
+#endif
 
 template <int D, int E, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
@@ -447,8 +470,9 @@ static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
         if (e != hipSuccess) return e;
     }
     if (stage < 0 || stage == 1) {
-        const int n_kt = (a.Nk + 127) / 128;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, E, CAUSAL>), dim3(BH * n_kt), dim3(256), 0, st, a.Q, a.K, a.V, a.dO,
+        constexpr int NW = FA_DKDV_WAVES;
+        const int n_kt = (a.Nk + 32 * NW - 1) / (32 * NW);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, E, CAUSAL>), dim3(BH * n_kt), dim3(NW * 64), 0, st, a.Q, a.K, a.V, a.dO,
                            a.LSE, a.Dvec, a.dK, a.dV, BH, a.Nq, a.Nk, a.scale, sl2, n_kt);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -482,7 +506,7 @@ hipError_t launch_bwd(const BwdArgs &a, int stage) {
 }
 
 const char *describe_bwd() {
-    return "bwd_pre_kernel (D=rowsum(dO*O)) -> bwd_dkdv_kernel<D, 4 waves x 32 keys, 64-row query steps, "
+    return "bwd_pre_kernel (D=rowsum(dO*O)) -> bwd_dkdv_kernel<D, 8 waves x 32 keys, 64-row query steps, "
            "double-buffered Q/dO, transposed LDS reads> -> bwd_dq_kernel<D, 8 waves x 32 rows, 64-key tiles>; "
            "no atomics";
 }
