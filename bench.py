@@ -125,15 +125,16 @@ def main():
     }
     dom = max(names, key=lambda n: kern_ms[n])
     bound, units = work[dom]
+    traffic = measured_traffic(w.name, dom)
     if bound == "mfma":
         achieved = units / (kern_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "flops_per_launch": units, "avg_launch_ms": kern_ms[dom]}
     else:
         achieved = units / (kern_ms[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": units,
+                "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "bytes_per_launch": units,
                 "avg_launch_ms": kern_ms[dom]}
 
     if args.copy_probe_mib > 0:
@@ -177,6 +178,32 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def kernel_source_sha256() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "tiled_online_softmax_03_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` (read + written) from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE record of this workload, scaled by the
+    same counters' reading of a known-size copy -- or None when there is no
+    record or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    k = rec.get("kernels", {}).get(kernel)
+    if k is None or rec.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    return k["read_bytes"] + k["write_bytes"]
 
 
 def cpu_baseline(w, inp, heads):
