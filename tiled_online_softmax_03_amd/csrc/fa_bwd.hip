@@ -12,9 +12,9 @@
 //
 // Three launches on the caller's stream, each a stage of fa_bwd_stage:
 //   0. bwd_pre_kernel   D = rowsum(dO * O) in fp32.
-//   1. bwd_dkdv_kernel  K/V-stationary: a workgroup owns 256 keys of one head
-//                       (8 waves, two per SIMD, 32 keys each; K rows in VGPRs,
-//                       V rows in LDS) and walks
+//   1. bwd_dkdv_kernel  K/V-stationary: a workgroup owns 128 keys of one head
+//                       (8 waves, two per SIMD: 4 key groups x 2 query halves;
+//                       K and V rows in LDS) and walks
 //                       the query tiles, recomputing S, P, dP and dS, and
 //                       accumulating dV^T += dO^T P and dK^T += Q^T dS in
 //                       registers.  Q and dO are staged row-major through LDS
@@ -69,31 +69,46 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const void *__restrict__ O
 }
 
 // ---------------------------------------------------------------- 1. dK, dV
-template <int D, int NW, int E, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
+// Eight waves = 4 key groups x 2 query halves.  Wave w owns keys
+// k0 + 32*(w % 4) .. +31 and, in every 64-row query step, rows 32*(w / 4) ..
+// +31 of it; the two waves of a key group (which share a SIMD) keep separate
+// dK^T / dV^T partial sums that are added through LDS at the end.  K and V
+// fragments are read from LDS, so no VGPRs hold them.
+template <int D, int E, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, const void *__restrict__ V,
                      const void *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Dvec,
                      void *__restrict__ dK, void *__restrict__ dV, int BH, int Nq, int Nk, float scale,
                      float scale_log2, int n_kt) {
-    constexpr int NT = NW * 64;
-    constexpr int BKC = 32 * NW;  // keys per workgroup
-    constexpr int BQ = 64;        // query rows per step
-    constexpr int NQB = BQ / 32;  // 32-row blocks per step
+    constexpr int NW = 8, NT = 512;
+    constexpr int NKG = 4;        // key groups
+    constexpr int BKC = 32 * NKG; // keys per workgroup
+    constexpr int BQ = 64;        // query rows per step (32 per query half)
     constexpr int NCH = D / 8;    // 16-byte chunks per row
     constexpr int NKS = D / 16;   // k-steps over the head dim
     constexpr int NDB = D / 32;   // 32-row blocks of dK^T / dV^T
     constexpr bool DMA = E != ELT_F32;  // 16-bit Q / dO go global -> LDS directly
     constexpr int CH_PER_T = DMA ? 1 : BQ * NCH / NT;  // register staging (fp32 -> bf16)
-    static_assert(BQ * NCH % NT == 0, "staging split");
+    static_assert(BQ * NCH % NT == 0 && BKC * NCH % NT == 0, "staging split");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * D];
-    __shared__ __attribute__((aligned(16))) uint16_t dOs[2][BQ * D];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[BKC * D];  // this workgroup's V rows
-    __shared__ __attribute__((aligned(16))) float lse2[2][BQ];
-    __shared__ __attribute__((aligned(16))) float dvec[2][BQ];
+    // Q/dO tiles (double-buffered), this workgroup's K and V rows, row statistics.
+    // After the loop the same space holds the query-half partial sums (needs
+    // NKG * 2 * NDB * 16 * 64 floats = 128 KiB for d = 128).
+    constexpr int QBYTES = 2 * 2 * BQ * D * 2, KVBYTES = 2 * BKC * D * 2, STATS = 2 * 2 * BQ * 4;
+    constexpr int XBYTES = NKG * 2 * NDB * 16 * 64 * 4;
+    constexpr int LDS_BYTES = (QBYTES + KVBYTES + STATS) > XBYTES ? (QBYTES + KVBYTES + STATS) : XBYTES;
+    __shared__ __attribute__((aligned(16))) unsigned char lds_raw[LDS_BYTES];
+    uint16_t (*Qs)[BQ * D] = reinterpret_cast<uint16_t (*)[BQ * D]>(lds_raw);
+    uint16_t (*dOs)[BQ * D] = reinterpret_cast<uint16_t (*)[BQ * D]>(lds_raw + 2 * BQ * D * 2);
+    uint16_t *Ks = reinterpret_cast<uint16_t *>(lds_raw + QBYTES);
+    uint16_t *Vs = reinterpret_cast<uint16_t *>(lds_raw + QBYTES + BKC * D * 2);
+    float (*lse2)[BQ] = reinterpret_cast<float (*)[BQ]>(lds_raw + QBYTES + KVBYTES);
+    float (*dvec)[BQ] = reinterpret_cast<float (*)[BQ]>(lds_raw + QBYTES + KVBYTES + 2 * BQ * 4);
+    float *xchg = reinterpret_cast<float *>(lds_raw);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, g = lane >> 5;
+    const int kg = wave % NKG, qh = wave / NKG;
 
     int bh, kt;
     if constexpr (CAUSAL) {
@@ -109,31 +124,24 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
     const int64_t q_head = (int64_t)bh * Nq * D;
     const int64_t k_head = (int64_t)bh * Nk * D;
     const int k0 = kt * BKC;
-    const int kw0 = k0 + wave * 32;  // first key of this wave
-    const int kw = kw0 + l32;        // this lane's key
-    const int kw_ld = kw < Nk ? kw : Nk - 1;
+    const int kw0 = k0 + kg * 32;  // first key of this wave
+    const int kw = kw0 + l32;      // this lane's key
 
     const int n_qt = (Nq + BQ - 1) / BQ;
     const int qt_begin = CAUSAL ? min(k0 / BQ, n_qt) : 0;  // earlier rows see none of these keys
 
-    // K rows of this lane's key as B operands (k = head-dim index 16*ks + 8*g + v), held
-    // in VGPRs; the workgroup's V rows go to LDS once and are read from there, which keeps
-    // the kernel under 256 VGPRs so every matrix product uses VGPR accumulators.  Both
-    // are loaded before any tile prefetch so waiting for them never waits on a prefetch.
-    u32x4_t kf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        u32x4_t kz = load8_operand<E>(K, k_head + (int64_t)kw_ld * D + 16 * ks + 8 * g);
-        if (kw >= Nk) kz = u32x4_t{0u, 0u, 0u, 0u};
-        kf[ks] = kz;
-    }
+    // ---- this workgroup's K and V rows into LDS (row-major, swizzled; zero past Nk)
 #pragma unroll
     for (int j = 0; j < BKC * NCH / NT; ++j) {
         const int i = tid + j * NT;
         const int row = i / NCH, c = i % NCH;
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (k0 + row < Nk) w = load8_operand<E>(V, k_head + (int64_t)(k0 + row) * D + c * 8);
-        *reinterpret_cast<u32x4_t *>(&Vs[tile_off<D>(row, c * 8)]) = w;
+        u32x4_t kz = {0u, 0u, 0u, 0u}, vz = {0u, 0u, 0u, 0u};
+        if (k0 + row < Nk) {
+            kz = load8_operand<E>(K, k_head + (int64_t)(k0 + row) * D + c * 8);
+            vz = load8_operand<E>(V, k_head + (int64_t)(k0 + row) * D + c * 8);
+        }
+        *reinterpret_cast<u32x4_t *>(&Ks[tile_off<D>(row, c * 8)]) = kz;
+        *reinterpret_cast<u32x4_t *>(&Vs[tile_off<D>(row, c * 8)]) = vz;
     }
 
     // ---- staging of one query tile
@@ -196,32 +204,31 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
     // One query tile; BUF (compile-time) is the LDS buffer it reads, so every LDS
     // address is a fixed offset from a per-lane base.
     auto step = [&](int qt, auto buf_c) {
-        const int buf = buf_c;
+        constexpr int buf = decltype(buf_c)::value;
         const bool more = qt + 1 < n_qt;
         if (more) load_tile(qt + 1, buf ^ 1);  // in flight during this step's math
         const uint16_t *qs = Qs[buf];
         const uint16_t *ds = dOs[buf];
+        const int q0 = qt * BQ + qh * 32;
 
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-            const int q0 = qt * BQ + qb * 32;
-            if (CAUSAL && q0 + 31 < kw0) continue;  // every row of the block precedes this wave's keys
-
+        if (!CAUSAL || q0 + 31 >= kw0) {  // else every row of the block precedes this wave's keys
             // S = Q K^T and dP = dO V^T: lane = key, register r -> query q0 + 8*(r/4) + 4*g + r%4
             f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const int off = tile_off<D>(qb * 32 + l32, 16 * ks + 8 * g);
-                const u32x4_t vb = *reinterpret_cast<const u32x4_t *>(&Vs[tile_off<D>(wave * 32 + l32, 16 * ks + 8 * g)]);
-                s = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&qs[off]), kf[ks], s);
-                dp = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&ds[off]), vb, dp);
+                const int qoff = tile_off<D>(qh * 32 + l32, 16 * ks + 8 * g);
+                const int koff = tile_off<D>(kg * 32 + l32, 16 * ks + 8 * g);
+                s = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&qs[qoff]),
+                               *reinterpret_cast<const u32x4_t *>(&Ks[koff]), s);
+                dp = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&ds[qoff]),
+                                *reinterpret_cast<const u32x4_t *>(&Vs[koff]), dp);
             }
             // P = exp2(s*c - LSE*log2e), dS = P (dP - D)
             uint32_t pp[8], dd[8];
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
-                const f32x4_t L4 = *reinterpret_cast<const f32x4_t *>(&lse2[buf][qb * 32 + 8 * rq + 4 * g]);
-                const f32x4_t D4 = *reinterpret_cast<const f32x4_t *>(&dvec[buf][qb * 32 + 8 * rq + 4 * g]);
+                const f32x4_t L4 = *reinterpret_cast<const f32x4_t *>(&lse2[buf][qh * 32 + 8 * rq + 4 * g]);
+                const f32x4_t D4 = *reinterpret_cast<const f32x4_t *>(&dvec[buf][qh * 32 + 8 * rq + 4 * g]);
                 float p[4], t[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -243,39 +250,50 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
                 const u32x4_t bs = {dd[4 * h], dd[4 * h + 1], dd[4 * h + 2], dd[4 * h + 3]};
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    dvT[db] = mfma_in<E>(tr_operand<D>(ds, qb * 32 + 16 * h, 32 * db, lane), bp, dvT[db]);
-                    dkT[db] = mfma_in<E>(tr_operand<D>(qs, qb * 32 + 16 * h, 32 * db, lane), bs, dkT[db]);
+                    dvT[db] = mfma_in<E>(tr_operand<D>(ds, qh * 32 + 16 * h, 32 * db, lane), bp, dvT[db]);
+                    dkT[db] = mfma_in<E>(tr_operand<D>(qs, qh * 32 + 16 * h, 32 * db, lane), bs, dkT[db]);
                 }
             }
-            // one 32-row block in flight at a time keeps S, dP, P and dS of a single
-            // block live, which lets the dK/dV accumulators stay in registers
-            __builtin_amdgcn_sched_barrier(0);
         }
         if (more) store_tile(buf ^ 1);
         wait_vmem();
         __syncthreads();
     };
-#if FA_DKDV_UNROLL
     for (int qt = qt_begin; qt < n_qt; qt += 2) {
         step(qt, std::integral_constant<int, 0>{});
         if (qt + 1 < n_qt) step(qt + 1, std::integral_constant<int, 1>{});
     }
-#else
-    for (int qt = qt_begin; qt < n_qt; ++qt) step(qt, (qt - qt_begin) & 1);
-#endif
 
-    // ---- dK = scale * (dK^T)^T, dV = (dV^T)^T: lane = key, register r -> head dim 32db + 8*(r/4) + 4*g + r%4
-    if (kw < Nk) {
+    // ---- add the two query halves' partial sums (LDS, lane-major: conflict-free)
+    __syncthreads();  // every wave is done with the tiles the exchange area overlays
+    float *x = xchg + (size_t)kg * (2 * NDB * 16 * 64);
+    if (qh == 1) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                x[((0 * NDB + db) * 16 + r) * 64 + lane] = dkT[db][r];
+                x[((1 * NDB + db) * 16 + r) * 64 + lane] = dvT[db][r];
+            }
+    }
+    __syncthreads();
+    if (qh == 0 && kw < Nk) {
+        // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane = key, register r -> head dim 32db + 8*(r/4) + 4*g + r%4
         const int64_t row = k_head + (int64_t)kw * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
+                float a[4], b[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * rq + i;
+                    a[i] = (dkT[db][r] + x[((0 * NDB + db) * 16 + r) * 64 + lane]) * scale;
+                    b[i] = dvT[db][r] + x[((1 * NDB + db) * 16 + r) * 64 + lane];
+                }
                 const int col = db * 32 + 8 * rq + 4 * g;
-                store4<E>(dK, row + col, dkT[db][4 * rq] * scale, dkT[db][4 * rq + 1] * scale,
-                          dkT[db][4 * rq + 2] * scale, dkT[db][4 * rq + 3] * scale);
-                store4<E>(dV, row + col, dvT[db][4 * rq], dvT[db][4 * rq + 1], dvT[db][4 * rq + 2],
-                          dvT[db][4 * rq + 3]);
+                store4<E>(dK, row + col, a[0], a[1], a[2], a[3]);
+                store4<E>(dV, row + col, b[0], b[1], b[2], b[3]);
             }
     }
 }
@@ -449,13 +467,6 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
 }
 
 constexpr int kDqKeys = 64;  // keys per tile of the dQ pass
-#ifndef FA_DKDV_UNROLL
-#define FA_DKDV_UNROLL 1      // unroll the dK/dV query loop by two (immediate LDS offsets, more VGPRs)
-#endif
-#ifndef FA_DKDV_WAVES
-#define FA_DKDV_WAVES 8       // waves (32 keys each) per workgroup of the dK/dV pass
-#endif
-
 template <int D, int E, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
     hipStream_t st = (hipStream_t)a.stream;
@@ -470,9 +481,8 @@ static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
         if (e != hipSuccess) return e;
     }
     if (stage < 0 || stage == 1) {
-        constexpr int NW = FA_DKDV_WAVES;
-        const int n_kt = (a.Nk + 32 * NW - 1) / (32 * NW);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, E, CAUSAL>), dim3(BH * n_kt), dim3(NW * 64), 0, st, a.Q, a.K, a.V, a.dO,
+        const int n_kt = (a.Nk + 127) / 128;
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, E, CAUSAL>), dim3(BH * n_kt), dim3(512), 0, st, a.Q, a.K, a.V, a.dO,
                            a.LSE, a.Dvec, a.dK, a.dV, BH, a.Nq, a.Nk, a.scale, sl2, n_kt);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -506,7 +516,8 @@ hipError_t launch_bwd(const BwdArgs &a, int stage) {
 }
 
 const char *describe_bwd() {
-    return "bwd_pre_kernel (D=rowsum(dO*O)) -> bwd_dkdv_kernel<D, 8 waves x 32 keys, 64-row query steps, "
+    return "bwd_pre_kernel (D=rowsum(dO*O)) -> bwd_dkdv_kernel<D, 8 waves = 4 key groups x 2 query halves, "
+           "128 keys, 64-row query steps, "
            "double-buffered Q/dO, transposed LDS reads> -> bwd_dq_kernel<D, 8 waves x 32 rows, 64-key tiles>; "
            "no atomics";
 }
