@@ -149,7 +149,7 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
     const void *dOh = static_cast<const char *>(dO) + q_head * (E == ELT_F32 ? 4 : 2);
     u32x4_t qreg[CH_PER_T], dreg[CH_PER_T];
     float lreg = 0.f, dvreg = 0.f;
-    auto load_tile = [&](int qt, int buf) {
+    auto load_tile = [&](int qt, int buf) __attribute__((always_inline)) {
         const int q0 = qt * BQ;
         if constexpr (DMA) {
             dma_tile<D, BQ, NW>(Qh, q0, Nq, Qs[buf], wave, lane);
@@ -174,7 +174,7 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
             dvreg = qq < Nq ? Dvec[(int64_t)bh * Nq + qq] : 0.f;
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf) __attribute__((always_inline)) {
         if constexpr (!DMA) {
 #pragma unroll
             for (int j = 0; j < CH_PER_T; ++j) {
@@ -203,7 +203,7 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
 
     // One query tile; BUF (compile-time) is the LDS buffer it reads, so every LDS
     // address is a fixed offset from a per-lane base.
-    auto step = [&](int qt, auto buf_c) {
+    auto step = [&](int qt, auto buf_c) __attribute__((always_inline)) {
         constexpr int buf = decltype(buf_c)::value;
         const bool more = qt + 1 < n_qt;
         if (more) load_tile(qt + 1, buf ^ 1);  // in flight during this step's math
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
     const void *Kh = static_cast<const char *>(K) + k_head * (E == ELT_F32 ? 4 : 2);
     const void *Vh = static_cast<const char *>(V) + k_head * (E == ELT_F32 ? 4 : 2);
     u32x4_t kreg[CH_PER_T], vreg[CH_PER_T];
-    auto load_tile = [&](int k0, int buf) {
+    auto load_tile = [&](int k0, int buf) __attribute__((always_inline)) {
         if constexpr (DMA) {
             dma_tile<D, BC, NW>(Kh, k0, Nk, Ks[buf], wave, lane);
             dma_tile<D, BC, NW>(Vh, k0, Nk, Vs[buf], wave, lane);
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
             }
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf) __attribute__((always_inline)) {
         if constexpr (!DMA) {
 #pragma unroll
             for (int j = 0; j < CH_PER_T; ++j) {
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
     wait_vmem();
     __syncthreads();
 
-    auto step = [&](int kt, auto buf_c) {
+    auto step = [&](int kt, auto buf_c) __attribute__((always_inline)) {
         constexpr int buf = decltype(buf_c)::value;
         const int k0 = kt * BC;
         const bool more = kt + 1 < n_kt;

@@ -146,14 +146,21 @@ __device__ __forceinline__ void store4(void *base, int64_t elem, float a, float 
 }
 
 // Row-major 16-bit LDS tile with rows of W elements: 16-byte chunk c of row r
-// is stored at chunk c ^ swz<W>(r).  Eight consecutive rows read at one chunk
-// (ds_read_b128) and the 4-row x 32-byte blocks of a transposed read
-// (ds_read_b64_tr_b16) both land on distinct banks.
+// is stored at chunk c ^ swz<W>(r).  LDS has 64 four-byte banks (256 bytes).
+// Two access shapes must spread over them:
+//  * ds_read_b128 of one chunk from consecutive rows: swz is a bijection on
+//    the low row bits (16 rows for W = 128, 8 for W = 64);
+//  * ds_read_b64_tr_b16 of an 8-row x 64-byte block (rows r0 + 0..7, four
+//    aligned chunks): the rows must cover all four 64-byte bank groups.  For
+//    W = 128 a row is exactly 256 bytes, so the group is picked by swz bits 2-3
+//    and these come from row & 3; for W = 64 two rows share the 256 bytes and
+//    row & 1 selects the half, (row >> 1) & 1 the group inside it.
+// (A swizzle that keeps the 8 rows in two bank groups halves the transposed
+// read rate.)
 template <int W>
 __device__ __forceinline__ int swz(int row) {
-    int s = ((row & 3) << 1) | ((row >> 2) & 1);
-    if constexpr (W / 8 >= 16) s |= (row & 8);
-    return s;
+    if constexpr (W / 8 >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    return ((row & 3) << 1) | ((row >> 2) & 1);
 }
 
 // Element offset of (row, col) in such a tile; col must be a multiple of 4.

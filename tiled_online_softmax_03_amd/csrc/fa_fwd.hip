@@ -107,7 +107,7 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
     u32x4_t kreg[DMA ? 1 : KCH_PER_T];
     uint32_t vraw[VBLK_PER_T][4][2];  // [block][key][2 words of 4 columns] in the input type
     float vf32[E == ELT_F32 ? VBLK_PER_T : 1][4][4];
-    auto load_tile = [&](int k0, int buf) {
+    auto load_tile = [&](int k0, int buf) __attribute__((always_inline)) {
         if constexpr (DMA) {
             dma_tile<D, BC, NW>(Kh, k0, Nk, Ks[buf], wave, lane);
         } else {
@@ -121,7 +121,7 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
         }
         // Interior tiles (every key exists) take an unguarded path: a uniform branch
         // instead of one exec-masked load per key.
-        auto load_v = [&](auto guarded_c) {
+        auto load_v = [&](auto guarded_c) __attribute__((always_inline)) {
             constexpr bool guarded = decltype(guarded_c)::value;
 #pragma unroll
             for (int j = 0; j < VBLK_PER_T; ++j) {
@@ -148,7 +148,7 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
         if (k0 + BC <= Nk) load_v(std::false_type{});
         else load_v(std::true_type{});
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf) __attribute__((always_inline)) {
         if constexpr (!DMA) {
 #pragma unroll
             for (int j = 0; j < KCH_PER_T; ++j) {
@@ -203,7 +203,7 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
 
     // One key tile; BUF is the LDS buffer it reads (compile-time, so every LDS
     // address is a fixed offset from a per-lane base).
-    auto step = [&](int kt, auto buf_c) {
+    auto step = [&](int kt, auto buf_c) __attribute__((always_inline)) {
         constexpr int buf = decltype(buf_c)::value;
         const int k0 = kt * BC;
         const bool more = kt + 1 < n_kt;
