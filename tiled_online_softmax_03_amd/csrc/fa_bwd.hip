@@ -415,8 +415,20 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
                     s[kb] = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&Ks[buf][off]), qf[ks], s[kb]);
                     dp[kb] = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&Vs[buf][off]), df[ks], dp[kb]);
                 }
+            // masked scores -> -inf (P = 0), in a branch of its own taken only on the
+            // ragged or diagonal tile
             const bool ragged = k0 + BC > Nk;
             const bool diag = CAUSAL && (k0 + BC - 1 > q_wave0);
+            if (ragged || diag) {
+                keep_branch();
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * g + (r % 4);
+                        if (key >= Nk || (CAUSAL && key > q)) s[kb][r] = -INFINITY;
+                    }
+            }
             uint32_t dd[NKB][8];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
@@ -426,11 +438,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
                         const int r = 2 * i + e;
-                        float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -lse2));
-                        if (ragged || diag) {
-                            const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * g + (r % 4);
-                            if (key >= Nk || (CAUSAL && key > q)) pv = 0.f;
-                        }
+                        const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -lse2));
                         t[e] = pv * (dp[kb][r] - dv);
                     }
                     dd[kb][i] = pack_in<E>(t[0], t[1]);
