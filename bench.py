@@ -10,8 +10,10 @@ Prints ONE JSON line: whole-step throughput in TFLOP/s (forward counted as
 times, a roofline entry for the dominant kernel and a CPU baseline (the fp64
 oracle timed on a bounded sample of the same workload on this host).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload NAME]
                     [--no-cpu-baseline] [--cpu-heads 48] [--copy-probe-mib 0]
+                    [--no-sclk]
+    python bench.py --memory-sweep     (forward peak memory against N, one JSON line)
 """
 from __future__ import annotations
 
@@ -33,7 +35,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="train_b8h32n4096d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -41,6 +43,10 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size reference "
                          "for hardware byte counters)")
+    ap.add_argument("--no-sclk", action="store_true", help="skip sampling the graphics clock under load")
+    ap.add_argument("--memory-sweep", action="store_true",
+                    help="instead of the step benchmark: forward peak memory and time at B1 H32 d128 for "
+                         "N = 4096 .. 65536")
     return ap.parse_args()
 
 
@@ -56,6 +62,12 @@ def main():
     import synth
     import tiled_online_softmax_03_amd as fa
 
+    if args.memory_sweep:
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(2)
+        memory_sweep()
+        return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
@@ -105,6 +117,9 @@ def main():
             per[n].append(e[k].elapsed_time(e[k + 1]))
     kern_ms = {n: sum(v) / len(v) for n, v in per.items()}
     step_ms = (t1 - t0) * 1e3 / args.steps
+    step_events = [e[0].elapsed_time(e[-1]) for e in evs]  # fa_fwd start .. last backward stage end
+
+    sclk = None if args.no_sclk else sample_sclk(launch_step)
 
     F = w.fwd_flops()
     total_flops = 3.5 * F
@@ -170,7 +185,11 @@ def main():
         "bwd_tflops": bwd_tflops,
         "fwd_bwd_pct_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "kernel_ms": kern_ms,
+        "step_ms_events": spread(step_events),
+        "kernel_ms_spread": {n: spread(v) for n, v in per.items()},
         "peak_mem_bytes": peak_mem,
+        "sclk_mhz_under_load": sclk,
+        "versions": versions(torch),
         "describe": fa.fa_describe(w.d, fa.dtype_code(w.torch_dtype), w.causal),
         "device": torch.cuda.get_device_properties(0).gcnArchName,
         "torch": torch.__version__,
@@ -178,6 +197,125 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def spread(v):
+    """Median, min, max and interquartile range of a list of times (ms)."""
+    import statistics
+    v = sorted(v)
+    q = statistics.quantiles(v, n=4) if len(v) >= 2 else [v[0]] * 3
+    return {"median": statistics.median(v), "min": v[0], "max": v[-1], "iqr": q[2] - q[0], "n": len(v)}
+
+
+def sample_sclk(launch_step, seconds=4.0):
+    """Graphics clock (MHz, mean over the XCDs) read with amd-smi while the
+    step runs back to back; None when the tool is missing or says nothing."""
+    import re
+    import subprocess
+    import threading
+
+    import torch
+
+    out = {}
+
+    def query():
+        time.sleep(seconds / 3)
+        try:
+            r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True,
+                               timeout=seconds)
+            out["text"] = r.stdout
+        except Exception as e:  # tool absent or hung: no reading
+            out["error"] = repr(e)
+
+    th = threading.Thread(target=query)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end or th.is_alive():
+        for _ in range(10):
+            launch_step()
+        torch.cuda.synchronize()
+    th.join()
+    text = out.get("text", "")
+    # "gfx_<i>": {"clk": {"value": V, "unit": "MHz"}, ...}
+    vals = [float(m) for m in re.findall(r'"gfx_\d+":\s*\{\s*"clk":\s*\{\s*"value":\s*([0-9.]+)', text)]
+    if not vals:
+        return None
+    return {"mean": sum(vals) / len(vals), "min": min(vals), "max": max(vals), "xcds": len(vals),
+            "source": "amd-smi metric --clock"}
+
+
+def versions(torch):
+    import platform
+    import subprocess
+    v = {"torch": torch.__version__, "hip_runtime": torch.version.hip, "python": platform.python_version()}
+    try:
+        r = subprocess.run(["hipcc", "--version"], capture_output=True, text=True, timeout=60)
+        v["hipcc"] = " | ".join(l for l in r.stdout.splitlines() if l.startswith(("HIP version", "AMD clang")))
+    except Exception:
+        v["hipcc"] = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            v["rocm"] = f.read().strip()
+    except OSError:
+        v["rocm"] = None
+    p = torch.cuda.get_device_properties(0)
+    v["device"] = {"name": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+                   "memory_bytes": p.total_memory}
+    return v
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def memory_sweep():
+    """Forward-only peak device memory and time at B1 H32 d128, bf16,
+    non-causal, for N = 4096 .. 65536, against the size one materialised
+    bf16 score matrix would take."""
+    import torch
+
+    import synth
+    import tiled_online_softmax_03_amd as fa
+
+    fa.lib()
+    dev = torch.device("cuda:0")
+    rows = []
+    for n in (4096, 8192, 16384, 32768, 65536):
+        torch.cuda.empty_cache()
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        inp = synth.make_inputs(1, 32, n, n, 128, "bf16", seed=7000 + n, device=dev, with_dO=False)
+        Q, K, V = inp["Q"], inp["K"], inp["V"]
+        O = torch.empty_like(Q)
+        LSE = torch.empty((1, 32, n), device=dev, dtype=torch.float32)
+        scale = 128 ** -0.5
+        stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()  # from here on: what the forward itself needs
+        fa.fa_fwd(Q, K, V, O, LSE, scale, False, stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        reps = 3
+        for _ in range(reps):
+            fa.fa_fwd(Q, K, V, O, LSE, scale, False, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        ms = e0.elapsed_time(e1) / reps
+        flops = 4.0 * 32 * n * n * 128
+        rows.append({"N": n, "peak_bytes": peak, "inputs_outputs_bytes": 4 * 32 * n * 128 * 2 + 32 * n * 4,
+                     "materialised_S_bf16_bytes": 32 * n * n * 2, "fwd_ms": ms, "fwd_tflops": flops / ms / 1e9})
+        del inp, Q, K, V, O, LSE
+    print(json.dumps({"memory_sweep": "fa_fwd, B1 H32 d128 bf16, non-causal", "rows": rows,
+                      "device": torch.cuda.get_device_properties(0).gcnArchName}), flush=True)
 
 
 def kernel_source_sha256() -> str:
@@ -226,7 +364,9 @@ def cpu_baseline(w, inp, heads):
     dt = time.perf_counter() - t0
     flops = heads * 3.5 * w.fwd_flops() / BH
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": o.num_threads(), "kind": "oracle",
-            "sample": "%d of %d heads of %s, forward + backward, fp64, %.2f s" % (heads, BH, w.name, dt)}
+            "sample": "%d of %d heads of %s, forward + backward, fp64, %.2f s" % (heads, BH, w.name, dt),
+            "seconds": dt, "gflops_fp64_effective": flops / dt / 1e9, "host_cpus": os.cpu_count(),
+            "cpu_model": cpu_model()}
 
 
 if __name__ == "__main__":
