@@ -44,6 +44,11 @@ def parse():
                     help="also run one plain device copy of this many MiB (a known-size reference "
                          "for hardware byte counters)")
     ap.add_argument("--no-sclk", action="store_true", help="skip sampling the graphics clock under load")
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="time the forward alone (implied for workloads that have no backward)")
+    ap.add_argument("--splits", default=None,
+                    help="forward through fa_fwd_splitkv with this many key ranges ('auto' = "
+                         "fa_fwd_num_splits); implies --fwd-only")
     ap.add_argument("--memory-sweep", action="store_true",
                     help="instead of the step benchmark: forward peak memory and time at B1 H32 d128 for "
                          "N = 4096 .. 65536")
@@ -73,22 +78,33 @@ def main():
         sys.exit(2)
     fa.lib()
     w = synth.WORKLOADS[args.workload]
-    if not w.backward:
-        w = w.with_(backward=True)
+    fwd_only = args.fwd_only or args.splits is not None or not w.backward
     dev = torch.device("cuda:0")
-    inp = synth.workload_inputs(w, device=dev, with_dO=True)
-    Q, K, V, dO = inp["Q"], inp["K"], inp["V"], inp["dO"]
+    inp = synth.workload_inputs(w, device=dev, with_dO=not fwd_only)
+    Q, K, V, dO = inp["Q"], inp["K"], inp["V"], inp.get("dO")
     O = torch.empty_like(Q)
     LSE = torch.empty((w.B, w.H, w.Nq), device=dev, dtype=torch.float32)
-    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
-    ws = fa.alloc_workspace(Q, K)
     stream = torch.cuda.current_stream()
-    nst = fa.fa_bwd_num_stages()
+    splits = None
+    if args.splits is not None:
+        splits = (fa.fa_fwd_num_splits(w.B, w.H, w.Nq, w.Nk, w.d, w.causal) if args.splits == "auto"
+                  else int(args.splits))
+        nws = fa.fa_fwd_splitkv_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, splits)
+        split_ws = torch.empty(max(nws, 1), device=dev, dtype=torch.uint8) if nws > 0 else None
+    if fwd_only:
+        nst = 0
+    else:
+        dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+        ws = fa.alloc_workspace(Q, K)
+        nst = fa.fa_bwd_num_stages()
 
     def launch_step(events=None):
         if events is not None:
             events[0].record(stream)
-        fa.fa_fwd(Q, K, V, O, LSE, w.scale, w.causal, stream)
+        if splits is None:
+            fa.fa_fwd(Q, K, V, O, LSE, w.scale, w.causal, stream)
+        else:
+            fa.fa_fwd_splitkv(Q, K, V, O, LSE, splits, split_ws, w.scale, w.causal, stream)
         if events is not None:
             events[1].record(stream)
         for s in range(nst):
@@ -122,11 +138,11 @@ def main():
     sclk = None if args.no_sclk else sample_sclk(launch_step)
 
     F = w.fwd_flops()
-    total_flops = 3.5 * F
+    total_flops = (1.0 if fwd_only else 3.5) * F
     value = total_flops / (step_ms * 1e-3) / 1e12
     fwd_tflops = F / (kern_ms["fwd_kernel"] * 1e-3) / 1e12
     bwd_ms = sum(kern_ms[n] for n in names[1:])
-    bwd_tflops = 2.5 * F / (bwd_ms * 1e-3) / 1e12
+    bwd_tflops = 2.5 * F / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 else None
 
     # algorithmic work per launch of each kernel
     elt = {"bf16": 2, "f16": 2, "f32": 4}[w.dtype]
@@ -140,10 +156,12 @@ def main():
     }
     dom = max(names, key=lambda n: kern_ms[n])
     bound, units = work[dom]
-    traffic = measured_traffic(w.name, dom)
+    traffic = measured_traffic(w.name, dom) if splits is None else None
     if bound == "mfma":
         achieved = units / (kern_ms[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+        roof = {"bound": "mfma",
+                "kernel": dom if splits is None else "fwd_kernel (split ranges) + fwd_merge_kernel",
+                "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "flops_per_launch": units, "avg_launch_ms": kern_ms[dom]}
     else:
@@ -163,7 +181,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inp, args.cpu_heads)
+        cpu = cpu_baseline(w, inp, args.cpu_heads, fwd_only)
 
     out = {
         "metric": METRIC,
@@ -179,11 +197,13 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
-                   "causal": w.causal, "step": "fa_fwd + fa_bwd"},
+                   "causal": w.causal,
+                   "step": ("fa_fwd" if splits is None else "fa_fwd_splitkv(%d ranges)" % splits)
+                   + ("" if fwd_only else " + fa_bwd")},
         "fwd_tflops": fwd_tflops,
         "fwd_pct_peak": 100.0 * fwd_tflops / PEAK_BF16_TFLOPS,
         "bwd_tflops": bwd_tflops,
-        "fwd_bwd_pct_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "fwd_bwd_pct_peak": None if fwd_only else 100.0 * value / PEAK_BF16_TFLOPS,
         "kernel_ms": kern_ms,
         "step_ms_events": spread(step_events),
         "kernel_ms_spread": {n: spread(v) for n, v in per.items()},
@@ -318,6 +338,45 @@ def memory_sweep():
                       "device": torch.cuda.get_device_properties(0).gcnArchName}), flush=True)
 
 
+def cpu_baseline_fwd(w, inp, heads):
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    BH = w.B * w.H
+    o = oracle.load()
+    long = w.Nq * w.Nk > (1 << 26)  # a full head would take minutes: sampled rows
+    views = {}
+    for k in ("Q", "K", "V"):
+        t = inp[k].reshape(BH, 1, inp[k].shape[2], w.d)[:heads].to("cpu")
+        if t.dtype == torch.float32:
+            t = t.to(torch.bfloat16)
+        views[k] = t.double().numpy()
+    if long:
+        rows = synth.sample_rows(w.Nq, BH, 256)[:heads]
+        rr = np.array(rows)
+        t0 = time.perf_counter()
+        for h in range(heads):
+            o.fwd_rows(views["Q"][h:h + 1], views["K"][h:h + 1], views["V"][h:h + 1], rr[h:h + 1], w.scale, w.causal)
+        dt = time.perf_counter() - t0
+        # flops of the sampled rows: 4*d per allowed key
+        keys = sum((r + 1 if w.causal else w.Nk) for h in range(heads) for r in rows[h])
+        flops = 4.0 * w.d * keys
+        sample = "256 sampled query rows in each of %d of %d heads of %s, forward, fp64, %.2f s" % (
+            heads, BH, w.name, dt)
+    else:
+        t0 = time.perf_counter()
+        o.fwd(views["Q"], views["K"], views["V"], w.scale, w.causal)
+        dt = time.perf_counter() - t0
+        flops = heads * w.fwd_flops() / BH
+        sample = "%d of %d heads of %s, forward, fp64, %.2f s" % (heads, BH, w.name, dt)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": o.num_threads(), "kind": "oracle",
+            "sample": sample, "seconds": dt, "gflops_fp64_effective": flops / dt / 1e9,
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
 def kernel_source_sha256() -> str:
     import glob
     import hashlib
@@ -344,13 +403,17 @@ def measured_traffic(workload, kernel):
     return k["read_bytes"] + k["write_bytes"]
 
 
-def cpu_baseline(w, inp, heads):
-    """The fp64 oracle (fwd + analytic bwd, untiled) on the first `heads`
-    heads of the same inputs, timed on this host's cores."""
+def cpu_baseline(w, inp, heads, fwd_only=False):
+    """The fp64 oracle (fwd + analytic bwd, untiled; or the forward alone) on
+    the first `heads` heads of the same inputs -- for the long causal
+    workload, on 256 sampled rows of each of those heads -- timed on this
+    host's cores."""
     import oracle
 
     BH = w.B * w.H
     heads = max(1, min(heads, BH))
+    if fwd_only:
+        return cpu_baseline_fwd(w, inp, heads)
     views = {}
     for k in ("Q", "K", "V", "dO"):
         t = inp[k].reshape(BH, 1, inp[k].shape[2], w.d)[:heads]

@@ -74,6 +74,41 @@ fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LS
                  int dtype, void *stream);
 
 /*
+ * Split-KV forward: the same result as fa_fwd (O and LSE, up to rounding
+ * order) computed by cutting the keys into `num_splits` ranges of whole key
+ * tiles, one workgroup per (query tile, range), each producing the running
+ * state (m, l, u) of its range, followed by a merge of the states with the
+ * rule that combines key blocks (lumenova.space "research-attention",
+ * section 02: m* = max m_g, l = sum exp(m_g - m*) l_g, O = sum exp(m_g - m*)
+ * u_g / l).  For shapes with few query tiles -- a single head, a short
+ * query block against a long key sequence -- this fills the GPU where fa_fwd
+ * cannot.
+ *  - num_splits >= 1 and <= FA_MAX_SPLITS; 1 is exactly fa_fwd (workspace
+ *    unused, may be NULL).  Ranges past the last key are empty and harmless.
+ *  - workspace: caller-owned device memory of at least
+ *    fa_fwd_splitkv_workspace_size() bytes, 256-byte aligned, contents on
+ *    entry irrelevant, on return unspecified.  Layout: u [G][B*H*Nq][d]
+ *    float32, then m and l [G][B*H*Nq] float32 each, G = num_splits.
+ *  - Two launches on `stream` (partial states, merge); same argument rules
+ *    and errors as fa_fwd, plus FA_ERR_INVALID_ARG for a bad num_splits or a
+ *    short / misaligned workspace.
+ */
+#define FA_MAX_SPLITS 256
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits);
+fa_status fa_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                         int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                         int dtype, int num_splits, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
+ * A split count for fa_fwd_splitkv on one MI355X (256 CUs): 1 when fa_fwd
+ * already launches a workgroup per CU, otherwise enough ranges for about one
+ * workgroup per CU, keeping at least eight 64-key tiles per range.  Returns
+ * 0 for invalid sizes.
+ */
+int fa_fwd_num_splits(int B, int H, int Nq, int Nk, int d, int causal);
+
+/*
  * Bytes of device workspace fa_bwd needs for this shape: the float32 row
  * statistic D = rowsum(dO * O) [B,H,Nq], padded to 256 bytes.  Returns 0
  * for invalid sizes.

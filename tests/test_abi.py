@@ -26,7 +26,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
     assert names == ["fa_bwd", "fa_bwd_num_stages", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_describe",
-                     "fa_fwd", "fa_status_string"]
+                     "fa_fwd", "fa_fwd_num_splits", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+                     "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -121,3 +122,52 @@ def test_bwd_stages(lib):
     assert lib.fa_bwd_stage(-1, *args) == fa.FA_ERR_INVALID_ARG
     bad = (P, P, P, P, P, P, NULL, P, P, 1, 1, 8, 8, 64, 0.125, 0, 0, P, 1 << 40, NULL)
     assert lib.fa_bwd_stage(1, *bad) == fa.FA_ERR_INVALID_ARG
+
+
+def test_splitkv_workspace_size(lib):
+    B, H, Nq, Nk, d = 2, 3, 100, 50, 64
+    pad = lambda n: (n + 255) // 256 * 256
+    for G in (2, 5, 256):
+        rows = B * H * Nq * G
+        assert fa.fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, G) == pad(rows * d * 4) + 2 * pad(rows * 4)
+    assert fa.fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, 1) == 0  # one range is fa_fwd: no workspace
+    for G in (0, -3, 257):
+        assert fa.fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, G) == 0
+    assert fa.fa_fwd_splitkv_workspace_size(B, 0, Nq, Nk, d, 4) == 0
+
+
+def _split(lib, G=4, ws=P, ws_bytes=1 << 40, B=1, Q=P, d=64, scale=0.125):
+    return lib.fa_fwd_splitkv(Q, P, P, P, P, B, 1, 8, 8, d, scale, 0, 0, G, ws, ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(G=0), fa.FA_ERR_INVALID_ARG),
+    (dict(G=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(G=257), fa.FA_ERR_INVALID_ARG),
+    (dict(G=1, B=0), fa.FA_ERR_INVALID_ARG),          # one range: fa_fwd's own checks
+    (dict(ws=NULL), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=ctypes.c_void_p(0x10010)), fa.FA_ERR_INVALID_ARG),  # not 256-byte aligned
+    (dict(ws_bytes=256), fa.FA_ERR_INVALID_ARG),
+    (dict(Q=NULL), fa.FA_ERR_INVALID_ARG),
+    (dict(Q=MIS), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+])
+def test_splitkv_rejects(lib, kw, status):
+    assert _split(lib, **kw) == status
+
+
+def test_num_splits(lib):
+    # one head of 4096 queries: 16 query tiles -> 8 ranges of 8 key tiles
+    assert fa.fa_fwd_num_splits(1, 1, 4096, 4096, 64, False) == 8
+    # 32 heads of 128 queries against 32768 keys: 32 workgroups -> 8 ranges
+    assert fa.fa_fwd_num_splits(1, 32, 128, 32768, 128, False) == 8
+    # 4096 query tiles already fill 256 CUs
+    assert fa.fa_fwd_num_splits(8, 32, 4096, 4096, 128, False) == 1
+    assert fa.fa_fwd_num_splits(4, 16, 1024, 8192, 64, False) == 1
+    # a single query row against 8192 keys, 8 heads: 8 workgroups -> 16 ranges (8 tiles each)
+    assert fa.fa_fwd_num_splits(1, 8, 1, 8192, 128, False) == 16
+    # too few keys to split
+    assert fa.fa_fwd_num_splits(1, 1, 64, 100, 64, False) == 1
+    assert fa.fa_fwd_num_splits(0, 1, 64, 100, 64, False) == 0
+    assert fa.fa_fwd_num_splits(1, 1, 64, 100, 80, False) == 0

@@ -8,6 +8,9 @@ raises.
 Entry points keep the C names:
 
     fa_fwd(Q, K, V, O, LSE, scale, causal=False, stream=None)
+    fa_fwd_splitkv(Q, K, V, O, LSE, num_splits, workspace, scale, causal=False, stream=None)
+    fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, num_splits) -> int
+    fa_fwd_num_splits(B, H, Nq, Nk, d, causal) -> int
     fa_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal=False, stream=None)
     fa_bwd_workspace_size(B, H, Nq, Nk, d) -> int
     fa_bwd_num_stages() -> int
@@ -50,6 +53,12 @@ def lib() -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     L.fa_fwd.restype = i
+    L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    L.fa_fwd_splitkv.restype = i
+    L.fa_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i, i]
+    L.fa_fwd_splitkv_workspace_size.restype = sz
+    L.fa_fwd_num_splits.argtypes = [i, i, i, i, i, i]
+    L.fa_fwd_num_splits.restype = i
     L.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
     L.fa_bwd_workspace_size.restype = sz
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
@@ -112,6 +121,34 @@ def fa_fwd(Q, K, V, O, LSE, scale=None, causal=False, stream=None) -> None:
         raise FaError(st, "fa_fwd")
 
 
+def fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, num_splits) -> int:
+    return int(lib().fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, int(num_splits)))
+
+
+def fa_fwd_num_splits(B, H, Nq, Nk, d, causal=False) -> int:
+    return int(lib().fa_fwd_num_splits(B, H, Nq, Nk, d, int(bool(causal))))
+
+
+def fa_fwd_splitkv(Q, K, V, O, LSE, num_splits, workspace, scale=None, causal=False, stream=None) -> None:
+    B, H, Nq, Nk, d = _dims(Q, K)
+    for t in (Q, K, V, O, LSE):
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    _need(K.shape == V.shape and O.shape == Q.shape and tuple(LSE.shape) == (B, H, Nq), "shape mismatch")
+    _need(Q.dtype == K.dtype == V.dtype == O.dtype, "Q, K, V, O must share a dtype")
+    _need(str(LSE.dtype) == "torch.float32", "LSE must be float32")
+    if workspace is not None:
+        _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    wptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().fa_fwd_splitkv(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, H, Nq, Nk, d, float(scale),
+                              int(bool(causal)), dtype_code(Q.dtype), int(num_splits), wptr, nbytes,
+                              _stream_handle(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_splitkv")
+
+
 def fa_bwd_workspace_size(B, H, Nq, Nk, d) -> int:
     return int(lib().fa_bwd_workspace_size(B, H, Nq, Nk, d))
 
@@ -166,6 +203,21 @@ def forward(Q, K, V, scale=None, causal=False, stream=None):
     O = torch.empty_like(Q)
     LSE = torch.empty((B, H, Nq), device=Q.device, dtype=torch.float32)
     fa_fwd(Q, K, V, O, LSE, scale, causal, stream)
+    return O, LSE
+
+
+def forward_splitkv(Q, K, V, scale=None, causal=False, stream=None, num_splits=None):
+    """Allocate O, LSE and the split-KV workspace, run fa_fwd_splitkv (with
+    fa_fwd_num_splits' choice unless num_splits is given), return (O, LSE)."""
+    import torch
+    B, H, Nq, Nk, d = _dims(Q, K)
+    if num_splits is None:
+        num_splits = fa_fwd_num_splits(B, H, Nq, Nk, d, causal)
+    O = torch.empty_like(Q)
+    LSE = torch.empty((B, H, Nq), device=Q.device, dtype=torch.float32)
+    n = fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, num_splits)
+    ws = torch.empty(max(n, 1), device=Q.device, dtype=torch.uint8) if n > 0 else None
+    fa_fwd_splitkv(Q, K, V, O, LSE, num_splits, ws, scale, causal, stream)
     return O, LSE
 
 

@@ -45,6 +45,65 @@ fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LS
     return fa::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits) {
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || num_splits < 1 || num_splits > FA_MAX_SPLITS) return 0;
+    if (num_splits == 1) return 0;
+    const size_t rows = (size_t)B * H * Nq * (size_t)num_splits;
+    return pad256(rows * (size_t)d * sizeof(float)) + 2 * pad256(rows * sizeof(float));
+}
+
+fa_status fa_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H, int Nq,
+                         int Nk, int d, float scale, int causal, int dtype, int num_splits, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_INVALID_ARG;
+    if (num_splits == 1) return fa_fwd(Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, causal, dtype, stream);
+    if (!Q || !K || !V || !O || !LSE || !workspace) return FA_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+        return FA_ERR_INVALID_ARG;
+    if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_INVALID_ARG;
+    const fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    const size_t need = fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, num_splits);
+    if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+    const int BQ = fa::fwd_query_tile(), BC = fa::fwd_key_tile();
+    const int64_t grid = (int64_t)B * H * ((Nq + BQ - 1) / BQ) * num_splits;
+    if (grid >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
+    const size_t rows = (size_t)B * H * Nq * (size_t)num_splits;
+    char *ws = static_cast<char *>(workspace);
+    float *U = reinterpret_cast<float *>(ws);
+    float *M = reinterpret_cast<float *>(ws + pad256(rows * (size_t)d * sizeof(float)));
+    float *L = reinterpret_cast<float *>(ws + pad256(rows * (size_t)d * sizeof(float)) + pad256(rows * sizeof(float)));
+    const int n_kt = (Nk + BC - 1) / BC;
+    const int tiles_per_split = (n_kt + num_splits - 1) / num_splits;
+    fa::FwdArgs a{Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, causal ? 1 : 0, dtype, stream};
+    a.num_splits = num_splits;
+    a.keys_per_split = tiles_per_split * BC;
+    a.Upart = U;
+    a.Mpart = M;
+    a.Lpart = L;
+    return fa::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_num_splits(int B, int H, int Nq, int Nk, int d, int causal) {
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return 0;
+    (void)causal;
+    // Measured on MI355X (one head of 4096 x 4096, d64; 8 heads of one query
+    // against 8192 keys; 32 heads of 128 queries against 32768 keys): the
+    // best count gives about one workgroup per CU and keeps 8 or more key
+    // tiles per range; beyond that the extra prologues and the merge cost more
+    // than the added parallelism gains.
+    constexpr int kCUs = 256, kMinTilesPerSplit = 8;
+    const int BQ = fa::fwd_query_tile(), BC = fa::fwd_key_tile();
+    const int64_t wgs = (int64_t)B * H * ((Nq + BQ - 1) / BQ);
+    if (wgs >= kCUs) return 1;
+    const int n_kt = (Nk + BC - 1) / BC;
+    int64_t g = (kCUs + wgs - 1) / wgs;
+    const int64_t g_max = n_kt / kMinTilesPerSplit;
+    if (g > g_max) g = g_max;
+    if (g > FA_MAX_SPLITS) g = FA_MAX_SPLITS;
+    return g < 1 ? 1 : (int)g;
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d) {
     if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
     const size_t rows = (size_t)B * H * Nq;

@@ -24,6 +24,15 @@
 //    1e-3 relative-L2 budget; V converts from bf16 to fp16 exactly.
 //  * Softmax runs in base 2 with the scale folded into one FMA:
 //    p = exp2(s * scale*log2e - m2), m2 the running max in log2 units.
+//
+// Split-KV (SPLIT = true): the keys are cut into ranges of whole tiles, one
+// workgroup per (query tile, range), and each writes its unnormalised state
+// (u, m, l) for its rows instead of O and LSE; fwd_merge_kernel then combines
+// the ranges with the same merge rule the key loop applies tile by tile
+// (lumenova.space "research-attention", section 02): m* = max m_g,
+// l = sum 2^(m_g - m*) l_g, O = sum 2^(m_g - m*) u_g / l.  This gives shapes
+// with few query tiles (one head, or a short query block against a long key
+// sequence) enough workgroups for 256 CUs.
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -48,12 +57,27 @@ __device__ __forceinline__ int vtswz(int col) { return (col + col / (BC / 8)) % 
 // result beyond rounding.
 constexpr float kRescaleThreshold = 8.f;
 
-template <int D, int BC, int NW, int E, bool CAUSAL>
+// Starting value of the running maximum: finite, so that a row whose keys in
+// a range are all masked (possible under split-KV with the causal mask)
+// gives p = exp2(-inf - m) = 0 rather than exp2(-inf + inf) = NaN, and so
+// that the first real score always moves it (the accumulator is then
+// multiplied by exp2(-huge) = 0, which it already is).
+constexpr float kMaxInit = -3.402823466e38f;
+
+// Partial-state outputs of a split-KV launch: R = B*H*Nq rows, G ranges.
+struct SplitOut {
+    float *U;  // [G][R][D] unnormalised accumulator u
+    float *M;  // [G][R] running maximum, log2 units
+    float *L;  // [G][R] row sum l
+    int keys_per_split;  // a multiple of the key tile
+};
+
+template <int D, int BC, int NW, int E, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
                                                       const void *__restrict__ V, void *__restrict__ O,
                                                       float *__restrict__ LSE, int BH, int Nq, int Nk,
-                                                      float scale_log2, int n_qt) {
+                                                      float scale_log2, int n_qt, SplitOut part) {
     constexpr int BR = 32 * NW;    // query rows per workgroup
     constexpr int NT = NW * 64;    // threads
     constexpr int NCH = D / 8;     // 16-byte chunks per K row
@@ -73,8 +97,14 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, g = lane >> 5;
 
-    int bh, qt;
-    if constexpr (CAUSAL) {
+    int bh, qt, split = 0;
+    if constexpr (SPLIT) {
+        // key range outermost, so the workgroups of one range (same K/V rows) run together
+        const int L = blockIdx.x, per = BH * n_qt;
+        split = L / per;
+        bh = (L % per) / n_qt;
+        qt = (L % per) % n_qt;
+    } else if constexpr (CAUSAL) {
         // longest rows first: the last query tiles see the most keys
         const int L = blockIdx.x;
         qt = n_qt - 1 - L / BH;
@@ -93,7 +123,12 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
 
     int k_end = Nk;
     if constexpr (CAUSAL) k_end = min(Nk, min(qt * BR + BR, Nq));  // keys <= last query of the workgroup
-    const int n_kt = (k_end + BC - 1) / BC;
+    int k_begin = 0;
+    if constexpr (SPLIT) {
+        k_begin = split * part.keys_per_split;
+        k_end = min(k_end, k_begin + part.keys_per_split);
+    }
+    const int n_kt = k_end > k_begin ? (k_end - k_begin + BC - 1) / BC : 0;
 
     // Q^T fragments: B operand of S^T = K Q^T, k = head-dim index 16*ks + 8*g + v.
     // Loaded before any tile prefetch so waiting for them never waits on a prefetch.
@@ -193,11 +228,13 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
     f32x16_t o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x16_t{};
-    float m_used = -INFINITY, l_run = 0.f;
+    float m_used = kMaxInit, l_run = 0.f;
     const f16x2_t ones = {(_Float16)1.f, (_Float16)1.f};
 
-    load_tile(0, 0);
-    store_tile(0);
+    if (n_kt > 0) {  // (workgroup-uniform: an empty key range skips straight to the epilogue)
+        load_tile(k_begin, 0);
+        store_tile(0);
+    }
     wait_vmem();
     __syncthreads();
 
@@ -205,7 +242,7 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
     // address is a fixed offset from a per-lane base).
     auto step = [&](int kt, auto buf_c) __attribute__((always_inline)) {
         constexpr int buf = decltype(buf_c)::value;
-        const int k0 = kt * BC;
+        const int k0 = k_begin + kt * BC;
         const bool more = kt + 1 < n_kt;
         if (more) load_tile(k0 + BC, buf ^ 1);  // in flight during this tile's math
         if (!CAUSAL || k0 <= q_wave0 + 31) {  // else the tile lies above the diagonal for every row of this wave
@@ -289,8 +326,27 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
         if (kt + 1 < n_kt) step(kt + 1, std::integral_constant<int, 1>{});
     }
 
-    // ---- epilogue: O = u / l, LSE = (m_used + log2 l) * ln 2
     const float l_tot = half_sum(l_run);
+    if constexpr (SPLIT) {
+        // ---- partial state of this key range: u (unnormalised), m (log2 units), l
+        if (q < Nq) {
+            const int64_t R = (int64_t)BH * Nq;
+            const int64_t prow = (int64_t)split * R + (int64_t)bh * Nq + q;
+            float *urow = part.U + prow * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq)
+                    *reinterpret_cast<f32x4_t *>(urow + db * 32 + 8 * rq + 4 * g) =
+                        f32x4_t{o[db][4 * rq], o[db][4 * rq + 1], o[db][4 * rq + 2], o[db][4 * rq + 3]};
+            if (g == 0) {
+                part.M[prow] = m_used;
+                part.L[prow] = l_tot;
+            }
+        }
+        return;
+    }
+    // ---- epilogue: O = u / l, LSE = (m_used + log2 l) * ln 2
     const float inv = 1.f / l_tot;
     if (q < Nq) {
         const int64_t orow = q_head + (int64_t)q * D;
@@ -312,14 +368,57 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
 #define FA_FWD_KEYS 64
 #endif
 
+// Merge of the split-KV partial states: one thread per 4 columns of a row.
+template <int D, int E>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(SplitOut part, int G, int64_t R, void *__restrict__ O,
+                                                        float *__restrict__ LSE) {
+    constexpr int TPR = D / 4;       // threads per row
+    constexpr int RPB = 256 / TPR;   // rows per block
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int c4 = threadIdx.x % TPR;
+    if (row >= R) return;
+    // (unrolled so that the independent loads of several ranges are in flight together)
+    float m_star = kMaxInit;
+#pragma unroll 8
+    for (int gi = 0; gi < G; ++gi) m_star = fmaxf(m_star, part.M[gi * R + row]);
+    float l = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int gi = 0; gi < G; ++gi) {
+        const float a = __builtin_amdgcn_exp2f(part.M[gi * R + row] - m_star);
+        l = fmaf(a, part.L[gi * R + row], l);
+        const f32x4_t u = *reinterpret_cast<const f32x4_t *>(part.U + (gi * R + row) * D + 4 * c4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(a, u[e], acc[e]);
+    }
+    const float inv = 1.f / l;
+    store4<E>(O, row * D + 4 * c4, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    if (c4 == 0) LSE[row] = (m_star + __builtin_log2f(l)) * kLn2;
+}
+
 template <int D, int E, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs &a) {
     constexpr int BC = FA_FWD_KEYS, NW = FA_FWD_WAVES, BR = 32 * NW;
     const int n_qt = (a.Nq + BR - 1) / BR;
     const int BH = a.B * a.H;
-    const dim3 grid(BH * n_qt), block(NW * 64);
-    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, E, CAUSAL>), grid, block, 0, (hipStream_t)a.stream, a.Q, a.K, a.V,
-                       a.O, a.LSE, BH, a.Nq, a.Nk, a.scale * kLog2e, n_qt);
+    const dim3 block(NW * 64);
+    const float sl2 = a.scale * kLog2e;
+    hipStream_t st = (hipStream_t)a.stream;
+    if (a.num_splits <= 1) {
+        hipLaunchKernelGGL((fwd_kernel<D, BC, NW, E, CAUSAL, false>), dim3(BH * n_qt), block, 0, st, a.Q, a.K, a.V,
+                           a.O, a.LSE, BH, a.Nq, a.Nk, sl2, n_qt, SplitOut{});
+        return hipGetLastError();
+    }
+    const int G = a.num_splits;
+    const SplitOut part{a.Upart, a.Mpart, a.Lpart, a.keys_per_split};
+    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, E, CAUSAL, true>), dim3(BH * n_qt * G), block, 0, st, a.Q, a.K, a.V,
+                       a.O, a.LSE, BH, a.Nq, a.Nk, sl2, n_qt, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t R = (int64_t)BH * a.Nq;
+    constexpr int RPB = 256 / (D / 4);
+    hipLaunchKernelGGL((fwd_merge_kernel<D, E>), dim3((unsigned)((R + RPB - 1) / RPB)), dim3(256), 0, st, part, G,
+                       R, a.O, a.LSE);
     return hipGetLastError();
 }
 
@@ -338,6 +437,9 @@ static hipError_t launch_fwd_d(const FwdArgs &a) {
 }
 
 hipError_t launch_fwd(const FwdArgs &a) { return a.d == 64 ? launch_fwd_d<64>(a) : launch_fwd_d<128>(a); }
+
+int fwd_key_tile() { return FA_FWD_KEYS; }
+int fwd_query_tile() { return 32 * FA_FWD_WAVES; }
 
 const char *describe_fwd() {
     return "fwd_kernel<D, BC=64, waves=8 (256 query rows, 32 per wave), double-buffered K/V^T in LDS, "

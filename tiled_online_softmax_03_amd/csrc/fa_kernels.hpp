@@ -15,6 +15,10 @@ struct FwdArgs {
     float scale;
     int causal, dtype;
     void *stream;
+    // split-KV: num_splits > 1 key ranges of keys_per_split keys (a multiple
+    // of fwd_key_tile()), partial states in caller workspace, then a merge
+    int num_splits = 1, keys_per_split = 0;
+    float *Upart = nullptr, *Mpart = nullptr, *Lpart = nullptr;
 };
 
 struct BwdArgs {
@@ -29,6 +33,8 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs &a);
+int fwd_key_tile();    // keys per tile of the forward's key loop
+int fwd_query_tile();  // query rows per forward workgroup
 constexpr int kBwdStages = 3;
 // stage < 0 runs every stage in order.
 hipError_t launch_bwd(const BwdArgs &a, int stage);
