@@ -81,8 +81,16 @@ class Oracle:
         lib.oracle_online_row.argtypes = [P, P, I64, I64, I64, I64, P, P, P]
         lib.oracle_tiled_fwd.argtypes = [P, P, P, I64, I64, I64, I64, I64, D, I, I64, P, P]
         lib.oracle_num_threads.argtypes = []
+        U32P = ctypes.POINTER(ctypes.c_uint32)
+        U8P = ctypes.POINTER(ctypes.c_uint8)
+        lib.oracle_philox4x32_10.argtypes = [U32P, U32P, U32P]
+        lib.oracle_philox4x32_10.restype = None
+        lib.oracle_dropout_keep.argtypes = [I64, I64, I64, I64, I, ctypes.c_uint64, U8P]
+        lib.oracle_fwd_dropout.argtypes = [P, P, P, I64, I64, I64, I64, I64, D, I, U8P, D, P, P]
+        lib.oracle_bwd_dropout.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, D, I, U8P, D, P, P, P, P, P]
         for name in ("oracle_fwd", "oracle_fwd_rows", "oracle_bwd", "oracle_online_row",
-                     "oracle_tiled_fwd", "oracle_num_threads"):
+                     "oracle_tiled_fwd", "oracle_num_threads", "oracle_dropout_keep", "oracle_fwd_dropout",
+                     "oracle_bwd_dropout"):
             getattr(lib, name).restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -162,6 +170,54 @@ class Oracle:
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
 
+    # ---- dropout (see oracle.c: inverted dropout on P, Philox4x32-10 keep mask)
+
+    def philox4x32_10(self, ctr, key):
+        """Philox4x32-10 of a 4-word counter and a 2-word key; returns 4 uint32."""
+        c = np.ascontiguousarray(ctr, dtype=np.uint32)
+        k = np.ascontiguousarray(key, dtype=np.uint32)
+        out = np.empty(4, dtype=np.uint32)
+        U32P = ctypes.POINTER(ctypes.c_uint32)
+        self.lib.oracle_philox4x32_10(c.ctypes.data_as(U32P), k.ctypes.data_as(U32P), out.ctypes.data_as(U32P))
+        return out
+
+    def dropout_keep(self, B, H, Nq, Nk, t: int, seed: int):
+        """uint8 keep mask [B, H, Nq, Nk] for drop threshold t (rate t/256)."""
+        keep = np.empty((B, H, Nq, Nk), dtype=np.uint8)
+        _check(self.lib.oracle_dropout_keep(B, H, Nq, Nk, int(t), ctypes.c_uint64(int(seed) & (2 ** 64 - 1)),
+                                            keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))),
+               "oracle_dropout_keep")
+        return keep
+
+    def fwd_dropout(self, Q, K, V, keep, keep_scale: float, scale: float, causal: bool = False):
+        """Forward with dropout on P under the given keep mask.  Returns (O, LSE)."""
+        Q, K, V = _f64(Q), _f64(K), _f64(V)
+        B, H, Nq, Nk, d = _shape(Q, K)
+        keep = np.ascontiguousarray(keep, dtype=np.uint8)
+        if keep.shape != (B, H, Nq, Nk):
+            raise ValueError("keep must be [B, H, Nq, Nk]")
+        O = np.empty((B, H, Nq, d))
+        LSE = np.empty((B, H, Nq))
+        _check(self.lib.oracle_fwd_dropout(_ptr(Q), _ptr(K), _ptr(V), B, H, Nq, Nk, d, float(scale),
+                                           int(bool(causal)), keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                           float(keep_scale), _ptr(O), _ptr(LSE)), "oracle_fwd_dropout")
+        return O, LSE
+
+    def bwd_dropout(self, Q, K, V, dO, keep, keep_scale: float, scale: float, causal: bool = False):
+        """Backward with dropout on P.  Returns (dQ, dK, dV, O, LSE)."""
+        Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+        B, H, Nq, Nk, d = _shape(Q, K)
+        keep = np.ascontiguousarray(keep, dtype=np.uint8)
+        if keep.shape != (B, H, Nq, Nk):
+            raise ValueError("keep must be [B, H, Nq, Nk]")
+        dQ, dK, dV = np.empty_like(Q), np.empty_like(K), np.empty_like(V)
+        O, LSE = np.empty_like(Q), np.empty((B, H, Nq))
+        _check(self.lib.oracle_bwd_dropout(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), B, H, Nq, Nk, d, float(scale),
+                                           int(bool(causal)), keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                           float(keep_scale), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(O), _ptr(LSE)),
+               "oracle_bwd_dropout")
+        return dQ, dK, dV, O, LSE
+
 
 def load() -> Oracle:
     """The oracle built from oracle.c (compiled on first use if absent)."""
@@ -195,3 +251,19 @@ def tiled_fwd(*a, **k):
 
 def num_threads() -> int:
     return load().num_threads()
+
+
+def philox4x32_10(*a, **k):
+    return load().philox4x32_10(*a, **k)
+
+
+def dropout_keep(*a, **k):
+    return load().dropout_keep(*a, **k)
+
+
+def fwd_dropout(*a, **k):
+    return load().fwd_dropout(*a, **k)
+
+
+def bwd_dropout(*a, **k):
+    return load().bwd_dropout(*a, **k)

@@ -164,6 +164,56 @@ int oracle_fwd_rows(const double *Q, const double *K, const double *V, int64_t B
 }
 
 /*
+ * Gradients of one head.  P: the softmax probabilities; Pv: the matrix that
+ * multiplied V in the forward (P itself, or P~ = Z P keep_scale under
+ * dropout); z: the dropout keep mask, or NULL for none.
+ *   dP = dO V^T (times Z keep_scale under dropout), r_i = sum_j P_ij dP_ij,
+ *   dS = P (dP - r), dQ = scale dS K, dK = scale dS^T Q, dV = Pv^T dO.
+ * dS is scratch [Nq][Nk].
+ */
+static void head_grads(const double *q, const double *k, const double *v, const double *go, int64_t Nq,
+                       int64_t Nk, int64_t d, double scale, const double *P, const double *Pv, const uint8_t *z,
+                       double keep_scale, double *dS, double *gq, double *gk, double *gv) {
+    /* dP = dO V^T, then dS = P (dP - r) row by row */
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < Nq; ++i) {
+        double *row = dS + i * Nk;
+        for (int64_t j = 0; j < Nk; ++j) {
+            const double g = dot(go + i * d, v + j * d, d);
+            row[j] = !z ? g : (z[i * Nk + j] ? g * keep_scale : 0.0);
+        }
+        double r = 0.0;
+        for (int64_t j = 0; j < Nk; ++j) r += P[i * Nk + j] * row[j];
+        for (int64_t j = 0; j < Nk; ++j) row[j] = P[i * Nk + j] * (row[j] - r);
+    }
+    /* dQ_i = scale sum_j dS_ij K_j */
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < Nq; ++i) {
+        double *g = gq + i * d;
+        for (int64_t c = 0; c < d; ++c) g[c] = 0.0;
+        for (int64_t j = 0; j < Nk; ++j) {
+            const double w = dS[i * Nk + j];
+            for (int64_t c = 0; c < d; ++c) g[c] += w * k[j * d + c];
+        }
+        for (int64_t c = 0; c < d; ++c) g[c] *= scale;
+    }
+    /* dK_j = scale sum_i dS_ij Q_i ; dV_j = sum_i Pv_ij dO_i */
+    #pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < Nk; ++j) {
+        double *a = gk + j * d, *b = gv + j * d;
+        for (int64_t c = 0; c < d; ++c) { a[c] = 0.0; b[c] = 0.0; }
+        for (int64_t i = 0; i < Nq; ++i) {
+            const double ws = dS[i * Nk + j], wp = Pv[i * Nk + j];
+            for (int64_t c = 0; c < d; ++c) {
+                a[c] += ws * q[i * d + c];
+                b[c] += wp * go[i * d + c];
+            }
+        }
+        for (int64_t c = 0; c < d; ++c) a[c] *= scale;
+    }
+}
+
+/*
  * Backward over all heads.  Given Q, K, V and the upstream gradient dO,
  * returns dQ, dK, dV (and, when non-NULL, O and LSE of the same forward).
  * Per head: P as in the forward, dP = dO V^T, r_i = sum_j P_ij dP_ij,
@@ -182,47 +232,11 @@ int oracle_bwd(const double *Q, const double *K, const double *V, const double *
     }
     for (int64_t bh = 0; bh < B * H; ++bh) {
         const double *q = Q + bh * Nq * d, *k = K + bh * Nk * d, *v = V + bh * Nk * d;
-        const double *go = dO + bh * Nq * d;
-        double *gq = dQ + bh * Nq * d, *gk = dK + bh * Nk * d, *gv = dV + bh * Nk * d;
-
         head_probs(q, k, Nq, Nk, d, scale, causal, P, lse);
         if (O) head_pv(P, v, Nq, Nk, d, O + bh * Nq * d);
         if (LSE) memcpy(LSE + bh * Nq, lse, sizeof(double) * (size_t)Nq);
-
-        /* dP = dO V^T, then dS = P (dP - r) row by row */
-        #pragma omp parallel for schedule(static)
-        for (int64_t i = 0; i < Nq; ++i) {
-            double *row = dS + i * Nk;
-            for (int64_t j = 0; j < Nk; ++j) row[j] = dot(go + i * d, v + j * d, d);
-            double r = 0.0;
-            for (int64_t j = 0; j < Nk; ++j) r += P[i * Nk + j] * row[j];
-            for (int64_t j = 0; j < Nk; ++j) row[j] = P[i * Nk + j] * (row[j] - r);
-        }
-        /* dQ_i = scale sum_j dS_ij K_j */
-        #pragma omp parallel for schedule(static)
-        for (int64_t i = 0; i < Nq; ++i) {
-            double *g = gq + i * d;
-            for (int64_t c = 0; c < d; ++c) g[c] = 0.0;
-            for (int64_t j = 0; j < Nk; ++j) {
-                const double w = dS[i * Nk + j];
-                for (int64_t c = 0; c < d; ++c) g[c] += w * k[j * d + c];
-            }
-            for (int64_t c = 0; c < d; ++c) g[c] *= scale;
-        }
-        /* dK_j = scale sum_i dS_ij Q_i ; dV_j = sum_i P_ij dO_i */
-        #pragma omp parallel for schedule(static)
-        for (int64_t j = 0; j < Nk; ++j) {
-            double *a = gk + j * d, *b = gv + j * d;
-            for (int64_t c = 0; c < d; ++c) { a[c] = 0.0; b[c] = 0.0; }
-            for (int64_t i = 0; i < Nq; ++i) {
-                const double ws = dS[i * Nk + j], wp = P[i * Nk + j];
-                for (int64_t c = 0; c < d; ++c) {
-                    a[c] += ws * q[i * d + c];
-                    b[c] += wp * go[i * d + c];
-                }
-            }
-            for (int64_t c = 0; c < d; ++c) a[c] *= scale;
-        }
+        head_grads(q, k, v, dO + bh * Nq * d, Nq, Nk, d, scale, P, P, NULL, 1.0, dS, dQ + bh * Nq * d,
+                   dK + bh * Nk * d, dV + bh * Nk * d);
     }
     free(P); free(dS); free(lse);
     return 0;
@@ -299,6 +313,119 @@ int oracle_tiled_fwd(const double *Q, const double *K, const double *V, int64_t 
         free(vv);
     }
     return err;
+}
+
+/*
+ * ---- Dropout on the attention probabilities.
+ *
+ * The pages leave dropout out of the derivation (research-attention, section
+ * 01) and ask that training comparisons use the same dropout probability over
+ * the same forward and backward range (section 06); they define nothing more.
+ * Reading used here: inverted dropout on P.  With keep mask Z (0/1) and
+ * keep_scale = 1 / (1 - rate):
+ *   P~ = Z * P * keep_scale,  O = P~ V,  LSE unchanged (the softmax itself is
+ *   not touched);
+ *   dV = P~^T dO,  dP = Z * (dO V^T) * keep_scale,  r_i = sum_j P_ij dP_ij,
+ *   dS = P (dP - r),  dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ * The mask is drawn from a counter-based generator so that the backward can
+ * draw it again instead of storing N x N bits: Philox4x32 with 10 rounds,
+ * from Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as
+ * 1, 2, 3" (SC 2011): a 4 x 32-bit counter, a 2 x 32-bit key; each round
+ * multiplies counter words 0 and 2 by fixed constants, keeps both halves of
+ * the 64-bit products, and mixes the high halves with the other two words
+ * and the key; the key is advanced by fixed Weyl increments between rounds.
+ *
+ * Element (bh, i, j) (bh = b*H + h, query i, key j) is decided by byte j mod 4
+ * (least significant first) of output word i mod 4 of
+ * Philox4x32-10(counter = (j div 4, i div 4, bh, 0), key = (seed low 32 bits,
+ * seed high 32 bits)); it is dropped when that byte is below t, the rate in
+ * 1/256 units (rate realised = t / 256).
+ */
+static const uint32_t kPhiloxMul0 = 0xD2511F53u, kPhiloxMul1 = 0xCD9E8D57u;
+static const uint32_t kPhiloxWeyl0 = 0x9E3779B9u, kPhiloxWeyl1 = 0xBB67AE85u;
+
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += kPhiloxWeyl0;
+            k1 += kPhiloxWeyl1;
+        }
+        const uint64_t p0 = (uint64_t)kPhiloxMul0 * c0;
+        const uint64_t p1 = (uint64_t)kPhiloxMul1 * c2;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* keep[bh][i][j] = 1 unless element (bh, i, j) is dropped at threshold t (0..255). */
+int oracle_dropout_keep(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int t, uint64_t seed, uint8_t *keep) {
+    if (!keep || B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || t < 0 || t > 255) return -1;
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    #pragma omp parallel for schedule(static)
+    for (int64_t bh = 0; bh < B * H; ++bh)
+        for (int64_t i = 0; i < Nq; ++i)
+            for (int64_t j = 0; j < Nk; ++j) {
+                const uint32_t ctr[4] = {(uint32_t)(j / 4), (uint32_t)(i / 4), (uint32_t)bh, 0u};
+                uint32_t w[4];
+                oracle_philox4x32_10(ctr, key, w);
+                const uint32_t byte = (w[i % 4] >> (8 * (j % 4))) & 0xffu;
+                keep[(bh * Nq + i) * Nk + j] = byte >= (uint32_t)t;
+            }
+    return 0;
+}
+
+/* Forward with dropout (see above): O = (Z * P * keep_scale) V, LSE of the undropped softmax. */
+int oracle_fwd_dropout(const double *Q, const double *K, const double *V, int64_t B, int64_t H,
+                       int64_t Nq, int64_t Nk, int64_t d, double scale, int causal,
+                       const uint8_t *keep, double keep_scale, double *O, double *LSE) {
+    if (!Q || !K || !V || !keep || !O || !LSE || bad_shape(B, H, Nq, Nk, d)) return -1;
+    double *P = (double *)malloc(sizeof(double) * (size_t)(Nq * Nk));
+    if (!P) return -2;
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const double *q = Q + bh * Nq * d, *k = K + bh * Nk * d, *v = V + bh * Nk * d;
+        const uint8_t *z = keep + bh * Nq * Nk;
+        head_probs(q, k, Nq, Nk, d, scale, causal, P, LSE + bh * Nq);
+        for (int64_t e = 0; e < Nq * Nk; ++e) P[e] = z[e] ? P[e] * keep_scale : 0.0;
+        head_pv(P, v, Nq, Nk, d, O + bh * Nq * d);
+    }
+    free(P);
+    return 0;
+}
+
+/* Backward with dropout (see above); O and LSE (of the same dropped forward) when non-NULL. */
+int oracle_bwd_dropout(const double *Q, const double *K, const double *V, const double *dO,
+                       int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, double scale, int causal,
+                       const uint8_t *keep, double keep_scale,
+                       double *dQ, double *dK, double *dV, double *O, double *LSE) {
+    if (!Q || !K || !V || !dO || !keep || !dQ || !dK || !dV || bad_shape(B, H, Nq, Nk, d)) return -1;
+    double *P = (double *)malloc(sizeof(double) * (size_t)(Nq * Nk));
+    double *Pd = (double *)malloc(sizeof(double) * (size_t)(Nq * Nk));
+    double *dS = (double *)malloc(sizeof(double) * (size_t)(Nq * Nk));
+    double *lse = (double *)malloc(sizeof(double) * (size_t)Nq);
+    if (!P || !Pd || !dS || !lse) {
+        free(P); free(Pd); free(dS); free(lse);
+        return -2;
+    }
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const double *q = Q + bh * Nq * d, *k = K + bh * Nk * d, *v = V + bh * Nk * d;
+        const uint8_t *z = keep + bh * Nq * Nk;
+        head_probs(q, k, Nq, Nk, d, scale, causal, P, lse);
+        for (int64_t e = 0; e < Nq * Nk; ++e) Pd[e] = z[e] ? P[e] * keep_scale : 0.0;
+        if (O) head_pv(Pd, v, Nq, Nk, d, O + bh * Nq * d);
+        if (LSE) memcpy(LSE + bh * Nq, lse, sizeof(double) * (size_t)Nq);
+        head_grads(q, k, v, dO + bh * Nq * d, Nq, Nk, d, scale, P, Pd, z, keep_scale, dS, dQ + bh * Nq * d,
+                   dK + bh * Nk * d, dV + bh * Nk * d);
+    }
+    free(P); free(Pd); free(dS); free(lse);
+    return 0;
 }
 
 int oracle_num_threads(void) {

@@ -303,4 +303,113 @@ def pin_rows_match_full(o):
             assert np.max(np.abs(Lr[t] - Lf[t, rows[t]])) <= 1e-14
 
 
+# ---------------------------------------------------------------- dropout (research-attention sections 01, 06)
+
+def pin_philox_known_answers(o):
+    """Philox4x32-10 reproduces the generator's published known-answer vectors."""
+    g = _golden("philox4x32_10_kat.json")
+    for v in g["vectors"]:
+        ctr = [int(x, 16) for x in v["ctr"]]
+        key = [int(x, 16) for x in v["key"]]
+        out = [int(x, 16) for x in v["out"]]
+        assert [int(x) for x in o.philox4x32_10(ctr, key)] == out, v
+
+
+def pin_dropout_rate(o):
+    """Threshold t drops a fraction t/256 of the elements (within 5 binomial
+    standard deviations over 2^18 elements); t = 0 drops nothing."""
+    n = 2 * 2 * 256 * 256
+    for t in (0, 26, 128, 255):
+        keep = o.dropout_keep(2, 2, 256, 256, t, 0x1234_5678_9abc)
+        frac = 1.0 - keep.mean()
+        if t == 0:
+            assert frac == 0.0
+        else:
+            p = t / 256.0
+            assert abs(frac - p) <= 5 * math.sqrt(p * (1 - p) / n), (t, frac)
+
+
+def pin_dropout_streams_distinct(o):
+    """Different heads, query rows, key columns and seeds draw different masks
+    (the counter separates every element; a mask shared between any two of
+    them would be a repeated stream)."""
+    keep = o.dropout_keep(1, 3, 16, 64, 128, 99).astype(np.int64)
+    for a, b in ((0, 1), (0, 2), (1, 2)):
+        assert np.mean(keep[0, a] == keep[0, b]) < 0.75
+    for i in range(15):  # neighbouring rows: within and across 4-row blocks
+        assert np.mean(keep[0, 0, i] == keep[0, 0, i + 1]) < 0.8, i
+    for j in range(63):
+        assert np.mean(keep[0, 0, :, j] == keep[0, 0, :, j + 1]) < 0.85, j
+    other = o.dropout_keep(1, 3, 16, 64, 128, 100).astype(np.int64)
+    assert np.mean(keep == other) < 0.6
+
+
+def pin_dropout_keep_all_is_plain(o):
+    """A mask that keeps everything with scale 1 gives exactly the plain forward and backward."""
+    for causal in (False, True):
+        Q, K, V, dO = _qkv(51 + causal, 1, 2, 9, 9, 4)
+        keep = np.ones((1, 2, 9, 9), dtype=np.uint8)
+        O1, L1 = o.fwd(Q, K, V, 0.6, causal)
+        O2, L2 = o.fwd_dropout(Q, K, V, keep, 1.0, 0.6, causal)
+        assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+        g1 = o.bwd(Q, K, V, dO, 0.6, causal)
+        g2 = o.bwd_dropout(Q, K, V, dO, keep, 1.0, 0.6, causal)
+        for a, b in zip(g1, g2):
+            assert np.array_equal(a, b)
+
+
+def pin_dropout_finite_differences(o):
+    """Under a fixed keep mask the dropped forward is differentiable: central
+    differences of L = sum(dO * O) agree with the dropout backward to 1e-6."""
+    h = 1e-6
+    for causal, (Nq, Nk, d), t in ((False, (5, 7, 3), 77), (True, (8, 8, 2), 128)):
+        Q, K, V, dO = _qkv(300 + Nq * Nk + causal, 1, 2, Nq, Nk, d)
+        keep = o.dropout_keep(1, 2, Nq, Nk, t, 4242)
+        ks = 256.0 / (256 - t)
+        scale = 0.8
+        dQ, dK, dV, O, L = o.bwd_dropout(Q, K, V, dO, keep, ks, scale, causal)
+        O2, _ = o.fwd_dropout(Q, K, V, keep, ks, scale, causal)
+        assert np.max(np.abs(O - O2)) <= 1e-14
+
+        def loss():
+            Ox, _ = o.fwd_dropout(Q, K, V, keep, ks, scale, causal)
+            return float(np.sum(dO * Ox))
+
+        for name, X, G in (("Q", Q, dQ), ("K", K, dK), ("V", V, dV)):
+            num = np.zeros_like(X)
+            for idx in np.ndindex(X.shape):
+                old = X[idx]
+                X[idx] = old + h
+                lp = loss()
+                X[idx] = old - h
+                lm = loss()
+                X[idx] = old
+                num[idx] = (lp - lm) / (2 * h)
+            err = np.linalg.norm(num - G) / max(np.linalg.norm(num), 1e-30)
+            assert err <= 1e-6, (name, causal, err)
+
+
+def pin_dropout_unbiased(o):
+    """Inverted dropout keeps the expectation: averaged over many seeds, the
+    dropped output approaches the plain one (the sample mean's error stays
+    within a few of its own standard errors)."""
+    Q, K, V = _qkv(61, 1, 1, 4, 32, 8, with_dO=False)
+    O, _ = o.fwd(Q, K, V, 0.5)
+    t, n = 128, 400
+    samples = np.stack([o.fwd_dropout(Q, K, V, o.dropout_keep(1, 1, 4, 32, t, s), 2.0, 0.5)[0] for s in range(n)])
+    mean, se = samples.mean(0), samples.std(0) / math.sqrt(n)
+    z = (mean - O) / se
+    assert np.sqrt(np.mean(z ** 2)) < 1.6, np.sqrt(np.mean(z ** 2))
+
+
+def pin_dropout_dK_sums_to_zero(o):
+    """Under dropout each row of dS still sums to zero (r is taken with the
+    undropped P), so sum_j dK_j = 0."""
+    for causal in (False, True):
+        Q, K, V, dO = _qkv(71 + causal, 1, 2, 12, 12, 4)
+        keep = o.dropout_keep(1, 2, 12, 12, 90, 7)
+        _, dK, _, _, _ = o.bwd_dropout(Q, K, V, dO, keep, 256.0 / 166, 0.6, causal)
+        assert np.max(np.abs(dK.sum(2))) <= 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -19,7 +19,7 @@ MUTANTS = [
     ("dK_no_scale", "a[c] *= scale;", "a[c] *= 1.0;"),
     ("dQ_uses_V", "g[c] += w * k[j * d + c];", "g[c] += w * v[j * d + c];"),
     ("dK_uses_P", "ws = dS[i * Nk + j], wp", "ws = P[i * Nk + j], wp"),
-    ("dV_uses_dS", "wp = P[i * Nk + j];", "wp = dS[i * Nk + j];"),
+    ("dV_uses_dS", "wp = Pv[i * Nk + j];", "wp = dS[i * Nk + j];"),
     ("dV_uses_Q", "b[c] += wp * go[i * d + c];", "b[c] += wp * q[i * d + c];"),
     ("mask_reversed", "return !causal || j <= i;", "return !causal || j >= i;"),
     ("mask_strict", "return !causal || j <= i;", "return !causal || j < i || j == 0;"),
@@ -31,6 +31,16 @@ MUTANTS = [
     ("online_alpha_sign", "const double alpha = exp(m - m_new);", "const double alpha = exp(m_new - m);"),
     ("online_p_old_max", "const double p = exp(s[j] - m_new);", "const double p = exp(s[j] - m);"),
     ("rows_no_mask", "if (!allowed(i, j, causal)) continue;\n                const double p", "const double p"),
+    ("philox_key_not_bumped", "            k1 += kPhiloxWeyl1;\n", "            k1 += 0u;\n"),
+    ("philox_hi_for_lo", "        c1 = lo1;", "        c1 = hi1;"),
+    ("dropout_keep_strict", "keep[(bh * Nq + i) * Nk + j] = byte >= (uint32_t)t;",
+     "keep[(bh * Nq + i) * Nk + j] = byte > (uint32_t)t;"),
+    ("dropout_word_by_key", "(w[i % 4] >> (8 * (j % 4)))", "(w[j % 4] >> (8 * (j % 4)))"),
+    ("dropout_counter_no_head", "(uint32_t)(i / 4), (uint32_t)bh, 0u}", "(uint32_t)(i / 4), 0u, 0u}"),
+    ("dropout_fwd_no_keep_scale", "P[e] = z[e] ? P[e] * keep_scale : 0.0;", "P[e] = z[e] ? P[e] : 0.0;"),
+    ("dropout_dP_no_keep_scale", "(z[i * Nk + j] ? g * keep_scale : 0.0)", "(z[i * Nk + j] ? g : 0.0)"),
+    ("dropout_dV_undropped", "scale, P, Pd, z, keep_scale,", "scale, P, P, z, keep_scale,"),
+    ("dropout_r_with_dropped_P", "r += P[i * Nk + j] * row[j];", "r += Pv[i * Nk + j] * row[j];"),
 ]
 
 
