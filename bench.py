@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--no-sclk", action="store_true", help="skip sampling the graphics clock under load")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time the forward alone (implied for workloads that have no backward)")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout rate on P (fa_fwd_dropout / fa_bwd_dropout; the backward is then timed as one "
+                         "call)")
+    ap.add_argument("--seed", type=int, default=1234, help="dropout seed")
     ap.add_argument("--splits", default=None,
                     help="forward through fa_fwd_splitkv with this many key ranges ('auto' = "
                          "fa_fwd_num_splits); implies --fwd-only")
@@ -91,24 +95,34 @@ def main():
                   else int(args.splits))
         nws = fa.fa_fwd_splitkv_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, splits)
         split_ws = torch.empty(max(nws, 1), device=dev, dtype=torch.uint8) if nws > 0 else None
+    drop = args.dropout > 0
+    if drop and splits is not None:
+        print("split-KV has no dropout variant", file=sys.stderr)
+        sys.exit(2)
     if fwd_only:
         nst = 0
     else:
         dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
         ws = fa.alloc_workspace(Q, K)
-        nst = fa.fa_bwd_num_stages()
+        nst = 1 if drop else fa.fa_bwd_num_stages()
 
     def launch_step(events=None):
         if events is not None:
             events[0].record(stream)
-        if splits is None:
+        if drop:
+            fa.fa_fwd_dropout(Q, K, V, O, LSE, args.dropout, args.seed, w.scale, w.causal, stream)
+        elif splits is None:
             fa.fa_fwd(Q, K, V, O, LSE, w.scale, w.causal, stream)
         else:
             fa.fa_fwd_splitkv(Q, K, V, O, LSE, splits, split_ws, w.scale, w.causal, stream)
         if events is not None:
             events[1].record(stream)
         for s in range(nst):
-            fa.fa_bwd_stage(s, Q, K, V, O, dO, LSE, dQ, dK, dV, ws, w.scale, w.causal, stream)
+            if drop:
+                fa.fa_bwd_dropout(Q, K, V, O, dO, LSE, dQ, dK, dV, ws, args.dropout, args.seed, w.scale, w.causal,
+                                  stream)
+            else:
+                fa.fa_bwd_stage(s, Q, K, V, O, dO, LSE, dQ, dK, dV, ws, w.scale, w.causal, stream)
             if events is not None:
                 events[2 + s].record(stream)
 
@@ -126,7 +140,8 @@ def main():
     t1 = time.perf_counter()
     peak_mem = torch.cuda.max_memory_allocated()
 
-    names = ["fwd_kernel"] + ["bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"][:nst]
+    names = ["fwd_kernel"] + (["fa_bwd_dropout (3 kernels)"] if drop else
+                              ["bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"][:nst])
     per = {n: [] for n in names}
     for e in evs:
         for k, n in enumerate(names):
@@ -153,10 +168,11 @@ def main():
         "bwd_pre_kernel": ("hbm", 2 * rows * w.d * elt + rows * 4),  # read O, dO; write D
         "bwd_dkdv_kernel": ("mfma", 2.0 * F),         # S, dP, dV, dK
         "bwd_dq_kernel": ("mfma", 1.5 * F),           # S, dP, dQ
+        "fa_bwd_dropout (3 kernels)": ("mfma", 2.5 * F),  # the whole backward, spec convention
     }
     dom = max(names, key=lambda n: kern_ms[n])
     bound, units = work[dom]
-    traffic = measured_traffic(w.name, dom) if splits is None else None
+    traffic = measured_traffic(w.name, dom) if splits is None and not drop else None
     if bound == "mfma":
         achieved = units / (kern_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma",
@@ -198,8 +214,9 @@ def main():
         "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal,
-                   "step": ("fa_fwd" if splits is None else "fa_fwd_splitkv(%d ranges)" % splits)
-                   + ("" if fwd_only else " + fa_bwd")},
+                   "step": ("fa_fwd_dropout(p=%g)" % args.dropout if drop else
+                            "fa_fwd" if splits is None else "fa_fwd_splitkv(%d ranges)" % splits)
+                   + ("" if fwd_only else " + fa_bwd_dropout" if drop else " + fa_bwd")},
         "fwd_tflops": fwd_tflops,
         "fwd_pct_peak": 100.0 * fwd_tflops / PEAK_BF16_TFLOPS,
         "bwd_tflops": bwd_tflops,

@@ -109,6 +109,34 @@ fa_status fa_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, f
 int fa_fwd_num_splits(int B, int H, int Nq, int Nk, int d, int causal);
 
 /*
+ * Attention with dropout on the probabilities (inverted dropout), for
+ * training runs that must keep the dropout rate over the same forward and
+ * backward range (lumenova.space "research-attention", section 06; the pages
+ * leave dropout out of the derivation itself, section 01):
+ *   O = (Z * P / (1 - rate)) V, LSE as without dropout;
+ *   the backward draws Z again and returns the gradients of that O.
+ * Z is not stored: element (b*H + h, query i, key j) is kept unless byte
+ * j % 4 of word i % 4 of Philox4x32-10 (Salmon et al., "Parallel Random
+ * Numbers: As Easy as 1, 2, 3", SC 2011) at counter (j / 4, i / 4, b*H + h, 0)
+ * with key (seed & 0xffffffff, seed >> 32) is below t, where
+ * t = fa_dropout_threshold(dropout_p); the realised rate is t / 256 and the
+ * survivors are scaled by 256 / (256 - t).  The same seed and shape give the
+ * same mask in fa_fwd_dropout and fa_bwd_dropout (and on every call).
+ *  - dropout_p in [0, 1), finite; t = 0 (dropout_p < 1/512) is exactly
+ *    fa_fwd / fa_bwd.  Otherwise FA_ERR_INVALID_ARG.
+ *  - Everything else as fa_fwd / fa_bwd (same workspace for the backward).
+ */
+int fa_dropout_threshold(float dropout_p); /* t in 0..255, or -1 if dropout_p is not in [0, 1) */
+fa_status fa_fwd_dropout(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                         int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                         float dropout_p, unsigned long long seed, void *stream);
+fa_status fa_bwd_dropout(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                         const float *LSE, void *dQ, void *dK, void *dV,
+                         int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                         float dropout_p, unsigned long long seed,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Bytes of device workspace fa_bwd needs for this shape: the float32 row
  * statistic D = rowsum(dO * O) [B,H,Nq], padded to 256 bytes.  Returns 0
  * for invalid sizes.

@@ -85,7 +85,7 @@ class Oracle:
         U8P = ctypes.POINTER(ctypes.c_uint8)
         lib.oracle_philox4x32_10.argtypes = [U32P, U32P, U32P]
         lib.oracle_philox4x32_10.restype = None
-        lib.oracle_dropout_keep.argtypes = [I64, I64, I64, I64, I, ctypes.c_uint64, U8P]
+        lib.oracle_dropout_keep.argtypes = [I64, I64, I64, I64, I, ctypes.c_uint64, I64, U8P]
         lib.oracle_fwd_dropout.argtypes = [P, P, P, I64, I64, I64, I64, I64, D, I, U8P, D, P, P]
         lib.oracle_bwd_dropout.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, D, I, U8P, D, P, P, P, P, P]
         for name in ("oracle_fwd", "oracle_fwd_rows", "oracle_bwd", "oracle_online_row",
@@ -181,11 +181,12 @@ class Oracle:
         self.lib.oracle_philox4x32_10(c.ctypes.data_as(U32P), k.ctypes.data_as(U32P), out.ctypes.data_as(U32P))
         return out
 
-    def dropout_keep(self, B, H, Nq, Nk, t: int, seed: int):
-        """uint8 keep mask [B, H, Nq, Nk] for drop threshold t (rate t/256)."""
+    def dropout_keep(self, B, H, Nq, Nk, t: int, seed: int, bh0: int = 0):
+        """uint8 keep mask [B, H, Nq, Nk] for drop threshold t (rate t/256), for
+        the B*H heads starting at flat head index bh0."""
         keep = np.empty((B, H, Nq, Nk), dtype=np.uint8)
         _check(self.lib.oracle_dropout_keep(B, H, Nq, Nk, int(t), ctypes.c_uint64(int(seed) & (2 ** 64 - 1)),
-                                            keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))),
+                                            int(bh0), keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))),
                "oracle_dropout_keep")
         return keep
 

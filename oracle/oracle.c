@@ -365,19 +365,24 @@ void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t
     out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
 }
 
-/* keep[bh][i][j] = 1 unless element (bh, i, j) is dropped at threshold t (0..255). */
-int oracle_dropout_keep(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int t, uint64_t seed, uint8_t *keep) {
-    if (!keep || B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || t < 0 || t > 255) return -1;
+/*
+ * keep[h][i][j] = 1 unless element (bh0 + h, i, j) is dropped at threshold t
+ * (0..255), for the B*H heads starting at head index bh0 (bh0 = 0: all heads
+ * of a [B,H] problem; bh0 > 0 with B = H = 1: one head of a larger problem).
+ */
+int oracle_dropout_keep(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int t, uint64_t seed, int64_t bh0,
+                        uint8_t *keep) {
+    if (!keep || B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || t < 0 || t > 255 || bh0 < 0) return -1;
     const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     #pragma omp parallel for schedule(static)
-    for (int64_t bh = 0; bh < B * H; ++bh)
+    for (int64_t h = 0; h < B * H; ++h)
         for (int64_t i = 0; i < Nq; ++i)
             for (int64_t j = 0; j < Nk; ++j) {
-                const uint32_t ctr[4] = {(uint32_t)(j / 4), (uint32_t)(i / 4), (uint32_t)bh, 0u};
+                const uint32_t ctr[4] = {(uint32_t)(j / 4), (uint32_t)(i / 4), (uint32_t)(bh0 + h), 0u};
                 uint32_t w[4];
                 oracle_philox4x32_10(ctr, key, w);
                 const uint32_t byte = (w[i % 4] >> (8 * (j % 4))) & 0xffu;
-                keep[(bh * Nq + i) * Nk + j] = byte >= (uint32_t)t;
+                keep[(h * Nq + i) * Nk + j] = byte >= (uint32_t)t;
             }
     return 0;
 }

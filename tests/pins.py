@@ -342,6 +342,9 @@ def pin_dropout_streams_distinct(o):
         assert np.mean(keep[0, 0, :, j] == keep[0, 0, :, j + 1]) < 0.85, j
     other = o.dropout_keep(1, 3, 16, 64, 128, 100).astype(np.int64)
     assert np.mean(keep == other) < 0.6
+    # one head of a larger problem is that problem's head bh0
+    one = o.dropout_keep(1, 1, 16, 64, 128, 99, bh0=2).astype(np.int64)
+    assert np.array_equal(one[0, 0], keep[0, 2])
 
 
 def pin_dropout_keep_all_is_plain(o):

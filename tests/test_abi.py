@@ -25,9 +25,9 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert names == ["fa_bwd", "fa_bwd_num_stages", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_describe",
-                     "fa_fwd", "fa_fwd_num_splits", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
-                     "fa_status_string"]
+    assert names == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_num_stages", "fa_bwd_stage", "fa_bwd_workspace_size",
+                     "fa_describe", "fa_dropout_threshold", "fa_fwd", "fa_fwd_dropout", "fa_fwd_num_splits",
+                     "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -171,3 +171,27 @@ def test_num_splits(lib):
     assert fa.fa_fwd_num_splits(1, 1, 64, 100, 64, False) == 1
     assert fa.fa_fwd_num_splits(0, 1, 64, 100, 64, False) == 0
     assert fa.fa_fwd_num_splits(1, 1, 64, 100, 80, False) == 0
+
+
+def test_dropout_threshold(lib):
+    # the rate is realised in 1/256 steps, rounded to nearest
+    assert fa.fa_dropout_threshold(0.0) == 0
+    assert fa.fa_dropout_threshold(0.0019) == 0    # below 1/512: no dropout
+    assert fa.fa_dropout_threshold(0.1) == 26      # 25.6 -> 26
+    assert fa.fa_dropout_threshold(0.5) == 128
+    assert fa.fa_dropout_threshold(0.999) == 255   # capped: 255/256
+    for bad in (-0.1, 1.0, 1.5, float("nan"), float("inf")):
+        assert fa.fa_dropout_threshold(bad) == -1
+
+
+def test_dropout_rejects(lib):
+    u64 = ctypes.c_ulonglong(7)
+    fwd = lambda p, B=1: lib.fa_fwd_dropout(P, P, P, P, P, B, 1, 8, 8, 64, 0.125, 0, 0, p, u64, NULL)
+    assert fwd(-0.5) == fa.FA_ERR_INVALID_ARG
+    assert fwd(1.0) == fa.FA_ERR_INVALID_ARG
+    assert fwd(float("nan")) == fa.FA_ERR_INVALID_ARG
+    assert fwd(0.1, B=0) == fa.FA_ERR_INVALID_ARG
+    bwd = lambda p, ws=P: lib.fa_bwd_dropout(P, P, P, P, P, P, P, P, P, 1, 1, 8, 8, 64, 0.125, 0, 0, p, u64, ws,
+                                             1 << 40, NULL)
+    assert bwd(1.2) == fa.FA_ERR_INVALID_ARG
+    assert bwd(0.1, ws=NULL) == fa.FA_ERR_INVALID_ARG

@@ -33,10 +33,10 @@ MUTANTS = [
     ("rows_no_mask", "if (!allowed(i, j, causal)) continue;\n                const double p", "const double p"),
     ("philox_key_not_bumped", "            k1 += kPhiloxWeyl1;\n", "            k1 += 0u;\n"),
     ("philox_hi_for_lo", "        c1 = lo1;", "        c1 = hi1;"),
-    ("dropout_keep_strict", "keep[(bh * Nq + i) * Nk + j] = byte >= (uint32_t)t;",
-     "keep[(bh * Nq + i) * Nk + j] = byte > (uint32_t)t;"),
+    ("dropout_keep_strict", "keep[(h * Nq + i) * Nk + j] = byte >= (uint32_t)t;",
+     "keep[(h * Nq + i) * Nk + j] = byte > (uint32_t)t;"),
     ("dropout_word_by_key", "(w[i % 4] >> (8 * (j % 4)))", "(w[j % 4] >> (8 * (j % 4)))"),
-    ("dropout_counter_no_head", "(uint32_t)(i / 4), (uint32_t)bh, 0u}", "(uint32_t)(i / 4), 0u, 0u}"),
+    ("dropout_counter_no_head", "(uint32_t)(i / 4), (uint32_t)(bh0 + h), 0u}", "(uint32_t)(i / 4), 0u, 0u}"),
     ("dropout_fwd_no_keep_scale", "P[e] = z[e] ? P[e] * keep_scale : 0.0;", "P[e] = z[e] ? P[e] : 0.0;"),
     ("dropout_dP_no_keep_scale", "(z[i * Nk + j] ? g * keep_scale : 0.0)", "(z[i * Nk + j] ? g : 0.0)"),
     ("dropout_dV_undropped", "scale, P, Pd, z, keep_scale,", "scale, P, P, z, keep_scale,"),

@@ -11,6 +11,9 @@ Entry points keep the C names:
     fa_fwd_splitkv(Q, K, V, O, LSE, num_splits, workspace, scale, causal=False, stream=None)
     fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, num_splits) -> int
     fa_fwd_num_splits(B, H, Nq, Nk, d, causal) -> int
+    fa_dropout_threshold(dropout_p) -> int
+    fa_fwd_dropout(Q, K, V, O, LSE, dropout_p, seed, scale, causal=False, stream=None)
+    fa_bwd_dropout(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, dropout_p, seed, scale, causal=False, stream=None)
     fa_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal=False, stream=None)
     fa_bwd_workspace_size(B, H, Nq, Nk, d) -> int
     fa_bwd_num_stages() -> int
@@ -59,6 +62,13 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_splitkv_workspace_size.restype = sz
     L.fa_fwd_num_splits.argtypes = [i, i, i, i, i, i]
     L.fa_fwd_num_splits.restype = i
+    u64 = ctypes.c_ulonglong
+    L.fa_dropout_threshold.argtypes = [f]
+    L.fa_dropout_threshold.restype = i
+    L.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, f, u64, vp]
+    L.fa_fwd_dropout.restype = i
+    L.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, f, u64, vp, sz, vp]
+    L.fa_bwd_dropout.restype = i
     L.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
     L.fa_bwd_workspace_size.restype = sz
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
@@ -147,6 +157,41 @@ def fa_fwd_splitkv(Q, K, V, O, LSE, num_splits, workspace, scale=None, causal=Fa
                               _stream_handle(stream))
     if st != FA_OK:
         raise FaError(st, "fa_fwd_splitkv")
+
+
+def fa_dropout_threshold(dropout_p) -> int:
+    return int(lib().fa_dropout_threshold(float(dropout_p)))
+
+
+def _fwd_check(Q, K, V, O, LSE):
+    B, H, Nq, Nk, d = _dims(Q, K)
+    for t in (Q, K, V, O, LSE):
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    _need(K.shape == V.shape and O.shape == Q.shape and tuple(LSE.shape) == (B, H, Nq), "shape mismatch")
+    _need(Q.dtype == K.dtype == V.dtype == O.dtype, "Q, K, V, O must share a dtype")
+    _need(str(LSE.dtype) == "torch.float32", "LSE must be float32")
+    return B, H, Nq, Nk, d
+
+
+def fa_fwd_dropout(Q, K, V, O, LSE, dropout_p, seed, scale=None, causal=False, stream=None) -> None:
+    B, H, Nq, Nk, d = _fwd_check(Q, K, V, O, LSE)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_dropout(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, H, Nq, Nk, d, float(scale),
+                              int(bool(causal)), dtype_code(Q.dtype), float(dropout_p),
+                              ctypes.c_ulonglong(int(seed) & (2 ** 64 - 1)), _stream_handle(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_dropout")
+
+
+def fa_bwd_dropout(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, dropout_p, seed, scale=None, causal=False,
+                   stream=None) -> None:
+    args = list(_bwd_args(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal, stream))
+    # _bwd_args ends with (..., dtype, workspace, nbytes, stream): the rate and seed go before the workspace
+    head, tail = args[:17], args[17:]
+    st = lib().fa_bwd_dropout(*head, float(dropout_p), ctypes.c_ulonglong(int(seed) & (2 ** 64 - 1)), *tail)
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dropout")
 
 
 def fa_bwd_workspace_size(B, H, Nq, Nk, d) -> int:

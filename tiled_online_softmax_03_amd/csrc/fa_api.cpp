@@ -28,21 +28,48 @@ fa_status check_common(int B, int H, int Nq, int Nk, int d, float scale, int dty
     return FA_OK;
 }
 
+// Dropout parameters for a rate; t = 0 means none.
+fa::Dropout make_dropout(int t, unsigned long long seed) {
+    fa::Dropout dr{(uint32_t)(seed & 0xffffffffull), (uint32_t)(seed >> 32), (uint32_t)t, 1.f};
+    if (t > 0) dr.keep_scale = 256.f / (float)(256 - t);
+    return dr;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d);
 
-fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H, int Nq,
-                 int Nk, int d, float scale, int causal, int dtype, void *stream) {
+int fa_dropout_threshold(float dropout_p) {
+    if (!isfinite(dropout_p) || dropout_p < 0.f || dropout_p >= 1.f) return -1;
+    const int t = (int)floorf(dropout_p * 256.f + 0.5f);
+    return t > 255 ? 255 : t;
+}
+
+static fa_status fwd_impl(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H, int Nq,
+                          int Nk, int d, float scale, int causal, int dtype, fa::Dropout drop, void *stream) {
     if (!Q || !K || !V || !O || !LSE) return FA_ERR_INVALID_ARG;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
         return FA_ERR_INVALID_ARG;
     const fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
     if (st != FA_OK) return st;
     fa::FwdArgs a{Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, causal ? 1 : 0, dtype, stream};
+    a.drop = drop;
     return fa::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H, int Nq,
+                 int Nk, int d, float scale, int causal, int dtype, void *stream) {
+    return fwd_impl(Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, causal, dtype, make_dropout(0, 0), stream);
+}
+
+fa_status fa_fwd_dropout(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H, int Nq,
+                         int Nk, int d, float scale, int causal, int dtype, float dropout_p, unsigned long long seed,
+                         void *stream) {
+    const int t = fa_dropout_threshold(dropout_p);
+    if (t < 0) return FA_ERR_INVALID_ARG;
+    return fwd_impl(Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, causal, dtype, make_dropout(t, seed), stream);
 }
 
 size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits) {
@@ -113,7 +140,7 @@ size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d) {
 static fa_status bwd_impl(int stage, const void *Q, const void *K, const void *V, const void *O, const void *dO,
                           const float *LSE, void *dQ, void *dK, void *dV, int B, int H, int Nq, int Nk, int d,
                           float scale, int causal, int dtype, void *workspace, size_t workspace_bytes,
-                          void *stream) {
+                          void *stream, fa::Dropout drop = make_dropout(0, 0)) {
     if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV || !workspace) return FA_ERR_INVALID_ARG;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(LSE) ||
         !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
@@ -124,7 +151,18 @@ static fa_status bwd_impl(int stage, const void *Q, const void *K, const void *V
     if (workspace_bytes < fa_bwd_workspace_size(B, H, Nq, Nk, d)) return FA_ERR_INVALID_ARG;
     float *Dvec = static_cast<float *>(workspace);
     fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal ? 1 : 0, dtype, Dvec, stream};
+    a.drop = drop;
     return fa::launch_bwd(a, stage) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_bwd_dropout(const void *Q, const void *K, const void *V, const void *O, const void *dO, const float *LSE,
+                         void *dQ, void *dK, void *dV, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                         int dtype, float dropout_p, unsigned long long seed, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    const int t = fa_dropout_threshold(dropout_p);
+    if (t < 0) return FA_ERR_INVALID_ARG;
+    return bwd_impl(-1, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal, dtype, workspace,
+                    workspace_bytes, stream, make_dropout(t, seed));
 }
 
 fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, const void *dO, const float *LSE,

@@ -26,6 +26,12 @@
 //                       dS^T, dQ^T += K^T dS^T.
 // dQ, dK and dV are therefore deterministic.  The price is that S and dP are
 // formed twice (7 matrix products instead of 5).
+//
+// Dropout (DROP = true): with keep flags Z drawn again from the counter-based
+// generator the forward used (fa_common.hpp), dV takes P~ = Z P / (1 - rate),
+// dP becomes Z (dO V^T) / (1 - rate), and dS = P (dP - D) with the undropped
+// P; D = rowsum(dO * O) still equals sum_j P_ij dP_ij because O is the
+// dropped forward's output.
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -74,12 +80,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const void *__restrict__ O
 // +31 of it; the two waves of a key group (which share a SIMD) keep separate
 // dK^T / dV^T partial sums that are added through LDS at the end.  K and V
 // fragments are read from LDS, so no VGPRs hold them.
-template <int D, int E, bool CAUSAL>
+template <int D, int E, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, const void *__restrict__ V,
                      const void *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Dvec,
                      void *__restrict__ dK, void *__restrict__ dV, int BH, int Nq, int Nk, float scale,
-                     float scale_log2, int n_kt) {
+                     float scale_log2, int n_kt, Dropout dr) {
     constexpr int NW = 8, NT = 512;
     constexpr int NKG = 4;        // key groups
     constexpr int BKC = 32 * NKG; // keys per workgroup
@@ -229,14 +235,22 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
             for (int rq = 0; rq < 4; ++rq) {
                 const f32x4_t L4 = *reinterpret_cast<const f32x4_t *>(&lse2[buf][qh * 32 + 8 * rq + 4 * g]);
                 const f32x4_t D4 = *reinterpret_cast<const f32x4_t *>(&dvec[buf][qh * 32 + 8 * rq + 4 * g]);
+                uint32_t keep = 0xfu;  // bit i: query q0 + 8rq + 4g + i survives dropout for this key
+                if constexpr (DROP) keep = dropout_keep_queries(dr, (uint32_t)bh, (uint32_t)(q0 + 8 * rq + 4 * g), (uint32_t)kw);
                 float p[4], t[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 4 * rq + i;
                     float pv = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -L4[i]));
                     if (CAUSAL && kw > q0 + 8 * rq + 4 * g + i) pv = 0.f;
-                    p[i] = pv;
-                    t[i] = pv * (dp[r] - D4[i]);
+                    if constexpr (DROP) {
+                        const bool kept = (keep >> i) & 1u;
+                        p[i] = kept ? pv * dr.keep_scale : 0.f;
+                        t[i] = pv * ((kept ? dp[r] * dr.keep_scale : 0.f) - D4[i]);
+                    } else {
+                        p[i] = pv;
+                        t[i] = pv * (dp[r] - D4[i]);
+                    }
                 }
                 pp[2 * rq] = pack_in<E>(p[0], p[1]);
                 pp[2 * rq + 1] = pack_in<E>(p[2], p[3]);
@@ -299,12 +313,12 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
 }
 
 // ---------------------------------------------------------------- 2. dQ
-template <int D, int BC, int E, bool CAUSAL>
+template <int D, int BC, int E, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q, const void *__restrict__ K,
                                                      const void *__restrict__ V, const void *__restrict__ dO,
                                                      const float *__restrict__ LSE, const float *__restrict__ Dvec,
                                                      void *__restrict__ dQ, int BH, int Nq, int Nk, float scale,
-                                                     float scale_log2, int n_qt) {
+                                                     float scale_log2, int n_qt, Dropout dr) {
     constexpr int NW = 8, NT = 512;
     constexpr int BR = 32 * NW;   // query rows per workgroup
     constexpr int NKB = BC / 32;  // 32-key blocks per tile
@@ -431,7 +445,15 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
             }
             uint32_t dd[NKB][8];
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+            for (int kb = 0; kb < NKB; ++kb) {
+                uint32_t keep = 0xffffu;  // bit r: register r of this block survives dropout
+                if constexpr (DROP) {
+                    keep = 0;
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq)
+                        keep |= dropout_keep_keys(dr, (uint32_t)bh, (uint32_t)q, (uint32_t)(k0 + 32 * kb + 8 * rq + 4 * g))
+                                << (4 * rq);
+                }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     float t[2];
@@ -439,10 +461,14 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
                     for (int e = 0; e < 2; ++e) {
                         const int r = 2 * i + e;
                         const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -lse2));
-                        t[e] = pv * (dp[kb][r] - dv);
+                        if constexpr (DROP)
+                            t[e] = pv * (((keep >> r) & 1u ? dp[kb][r] * dr.keep_scale : 0.f) - dv);
+                        else
+                            t[e] = pv * (dp[kb][r] - dv);
                     }
                     dd[kb][i] = pack_in<E>(t[0], t[1]);
                 }
+            }
             // dQ^T += K^T dS^T; k-step kst covers keys k0 + 16kst .. k0 + 16kst + 15
 #pragma unroll
             for (int kst = 0; kst < BC / 16; ++kst) {
@@ -488,17 +514,27 @@ static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    const bool drop = a.drop.t > 0;
     if (stage < 0 || stage == 1) {
         const int n_kt = (a.Nk + 127) / 128;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, E, CAUSAL>), dim3(BH * n_kt), dim3(512), 0, st, a.Q, a.K, a.V, a.dO,
-                           a.LSE, a.Dvec, a.dK, a.dV, BH, a.Nq, a.Nk, a.scale, sl2, n_kt);
+        if (drop)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, E, CAUSAL, true>), dim3(BH * n_kt), dim3(512), 0, st, a.Q, a.K, a.V,
+                               a.dO, a.LSE, a.Dvec, a.dK, a.dV, BH, a.Nq, a.Nk, a.scale, sl2, n_kt, a.drop);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, E, CAUSAL, false>), dim3(BH * n_kt), dim3(512), 0, st, a.Q, a.K, a.V,
+                               a.dO, a.LSE, a.Dvec, a.dK, a.dV, BH, a.Nq, a.Nk, a.scale, sl2, n_kt, Dropout{});
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (stage < 0 || stage == 2) {
         const int n_qt = (a.Nq + 255) / 256;
-        hipLaunchKernelGGL((bwd_dq_kernel<D, (E == ELT_F32 ? 32 : kDqKeys), E, CAUSAL>), dim3(BH * n_qt), dim3(512), 0, st, a.Q, a.K, a.V, a.dO,
-                           a.LSE, a.Dvec, a.dQ, BH, a.Nq, a.Nk, a.scale, sl2, n_qt);
+        constexpr int BC = E == ELT_F32 ? 32 : kDqKeys;
+        if (drop)
+            hipLaunchKernelGGL((bwd_dq_kernel<D, BC, E, CAUSAL, true>), dim3(BH * n_qt), dim3(512), 0, st, a.Q, a.K, a.V,
+                               a.dO, a.LSE, a.Dvec, a.dQ, BH, a.Nq, a.Nk, a.scale, sl2, n_qt, a.drop);
+        else
+            hipLaunchKernelGGL((bwd_dq_kernel<D, BC, E, CAUSAL, false>), dim3(BH * n_qt), dim3(512), 0, st, a.Q, a.K, a.V,
+                               a.dO, a.LSE, a.Dvec, a.dQ, BH, a.Nq, a.Nk, a.scale, sl2, n_qt, Dropout{});
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

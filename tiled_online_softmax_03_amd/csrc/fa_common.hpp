@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_types.hpp"
+
 namespace fa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -283,6 +285,55 @@ struct DmaPlan {
         }
     }
 };
+
+// ---- attention dropout (inverted dropout on P, the mask drawn again in the
+// backward).  The generator is Philox4x32 with 10 rounds from Salmon, Moraes,
+// Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC 2011):
+// per round, counter words 0 and 2 are multiplied by two fixed odd constants,
+// the high product halves are XORed with the other two words and the key,
+// the low halves carried over; the key moves by two Weyl increments between
+// rounds.  Element (bh, query i, key j) is decided by byte j % 4 (least
+// significant first) of word i % 4 of the output for counter
+// (j / 4, i / 4, bh, 0) and key (seed low, seed high): dropped when the byte
+// is below t (rate t / 256).  Parameters: struct Dropout (fa_types.hpp).
+__device__ __forceinline__ u32x4_t philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                 uint32_t k1) {
+    constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;    // multipliers of words 0 and 2
+    constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;  // key increments
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint32_t hiA = __umulhi(kMulA, c0), loA = kMulA * c0;
+        const uint32_t hiB = __umulhi(kMulB, c2), loB = kMulB * c2;
+        c0 = hiB ^ c1 ^ k0;
+        c1 = loB;
+        c2 = hiA ^ c3 ^ k1;
+        c3 = loA;
+        k0 += kWeylA;
+        k1 += kWeylB;
+    }
+    return u32x4_t{c0, c1, c2, c3};
+}
+
+// Keep flags (bit e set = keep) of keys j4 .. j4+3 for query i (j4 % 4 == 0).
+__device__ __forceinline__ uint32_t dropout_keep_keys(const Dropout &dr, uint32_t bh, uint32_t i, uint32_t j4) {
+    const u32x4_t w = philox4x32_10(j4 >> 2, i >> 2, bh, 0u, dr.k0, dr.k1);
+    const uint32_t s = i & 3u;
+    const uint32_t word = s == 0 ? w[0] : s == 1 ? w[1] : s == 2 ? w[2] : w[3];
+    uint32_t keep = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) keep |= (((word >> (8 * e)) & 0xffu) >= dr.t ? 1u : 0u) << e;
+    return keep;
+}
+
+// Keep flags (bit e set = keep) of queries i4 .. i4+3 for key j (i4 % 4 == 0).
+__device__ __forceinline__ uint32_t dropout_keep_queries(const Dropout &dr, uint32_t bh, uint32_t i4, uint32_t j) {
+    const u32x4_t w = philox4x32_10(j >> 2, i4 >> 2, bh, 0u, dr.k0, dr.k1);
+    const uint32_t sh = 8u * (j & 3u);
+    uint32_t keep = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) keep |= (((w[e] >> sh) & 0xffu) >= dr.t ? 1u : 0u) << e;
+    return keep;
+}
 
 // Map a hardware workgroup index to a logical one so that consecutive
 // logical indices land on the same XCD.  Workgroups are handed to the eight

@@ -33,6 +33,11 @@
 // l = sum 2^(m_g - m*) l_g, O = sum 2^(m_g - m*) u_g / l.  This gives shapes
 // with few query tiles (one head, or a short query block against a long key
 // sequence) enough workgroups for 256 CUs.
+//
+// Dropout (DROP = true): the row sum l takes the undropped P (the softmax is
+// not changed), the P V product takes P with the dropped elements zeroed,
+// and the epilogue multiplies by 1 / (1 - rate) together with 1 / l.  Each
+// lane draws the keep flags of its own query row, four keys per Philox call.
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -72,12 +77,13 @@ struct SplitOut {
     int keys_per_split;  // a multiple of the key tile
 };
 
-template <int D, int BC, int NW, int E, bool CAUSAL, bool SPLIT>
+template <int D, int BC, int NW, int E, bool CAUSAL, bool SPLIT, bool DROP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
                                                       const void *__restrict__ V, void *__restrict__ O,
                                                       float *__restrict__ LSE, int BH, int Nq, int Nk,
-                                                      float scale_log2, int n_qt, SplitOut part) {
+                                                      float scale_log2, int n_qt, SplitOut part, Dropout dr) {
+    static_assert(!(SPLIT && DROP), "split-KV has no dropout variant");
     constexpr int BR = 32 * NW;    // query rows per workgroup
     constexpr int NT = NW * 64;    // threads
     constexpr int NCH = D / 8;     // 16-byte chunks per K row
@@ -289,16 +295,28 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
             }
 
             // ---- P = exp2(s*c - m_used) rounded to fp16; l += sum of the rounded values
+            // (under dropout, pk then loses its dropped elements: l keeps them)
             uint32_t pk[NKB][8];
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+            for (int kb = 0; kb < NKB; ++kb) {
+                uint32_t keep = 0;  // bit r: register r of this block survives dropout
+                if constexpr (DROP) {
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq)
+                        keep |= dropout_keep_keys(dr, (uint32_t)bh, (uint32_t)q, (uint32_t)(k0 + 32 * kb + 8 * rq + 4 * g))
+                                << (4 * rq);
+                }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i], scale_log2, -m_used));
                     const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i + 1], scale_log2, -m_used));
                     pk[kb][i] = pack_f16(p0, p1);
                     l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk[kb][i]), ones, l_run, false);
+                    if constexpr (DROP)
+                        pk[kb][i] &= ((keep >> (2 * i)) & 1u ? 0x0000ffffu : 0u) |
+                                     ((keep >> (2 * i + 1)) & 1u ? 0xffff0000u : 0u);
                 }
+            }
 
             // ---- O^T += V^T P^T (fp16 matrix core).  k-step kst covers keys
             // 16*kst .. 16*kst+15; slot (g, v) holds key 16*kst + 4g + v (v < 4)
@@ -346,8 +364,8 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
         }
         return;
     }
-    // ---- epilogue: O = u / l, LSE = (m_used + log2 l) * ln 2
-    const float inv = 1.f / l_tot;
+    // ---- epilogue: O = u / l (times 1 / (1 - rate) under dropout), LSE = (m_used + log2 l) * ln 2
+    const float inv = (DROP ? dr.keep_scale : 1.f) / l_tot;
     if (q < Nq) {
         const int64_t orow = q_head + (int64_t)q * D;
 #pragma unroll
@@ -404,15 +422,20 @@ static hipError_t launch_fwd_t(const FwdArgs &a) {
     const dim3 block(NW * 64);
     const float sl2 = a.scale * kLog2e;
     hipStream_t st = (hipStream_t)a.stream;
+    if (a.drop.t > 0) {
+        hipLaunchKernelGGL((fwd_kernel<D, BC, NW, E, CAUSAL, false, true>), dim3(BH * n_qt), block, 0, st, a.Q, a.K,
+                           a.V, a.O, a.LSE, BH, a.Nq, a.Nk, sl2, n_qt, SplitOut{}, a.drop);
+        return hipGetLastError();
+    }
     if (a.num_splits <= 1) {
-        hipLaunchKernelGGL((fwd_kernel<D, BC, NW, E, CAUSAL, false>), dim3(BH * n_qt), block, 0, st, a.Q, a.K, a.V,
-                           a.O, a.LSE, BH, a.Nq, a.Nk, sl2, n_qt, SplitOut{});
+        hipLaunchKernelGGL((fwd_kernel<D, BC, NW, E, CAUSAL, false, false>), dim3(BH * n_qt), block, 0, st, a.Q, a.K,
+                           a.V, a.O, a.LSE, BH, a.Nq, a.Nk, sl2, n_qt, SplitOut{}, Dropout{});
         return hipGetLastError();
     }
     const int G = a.num_splits;
     const SplitOut part{a.Upart, a.Mpart, a.Lpart, a.keys_per_split};
-    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, E, CAUSAL, true>), dim3(BH * n_qt * G), block, 0, st, a.Q, a.K, a.V,
-                       a.O, a.LSE, BH, a.Nq, a.Nk, sl2, n_qt, part);
+    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, E, CAUSAL, true, false>), dim3(BH * n_qt * G), block, 0, st, a.Q, a.K,
+                       a.V, a.O, a.LSE, BH, a.Nq, a.Nk, sl2, n_qt, part, Dropout{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t R = (int64_t)BH * a.Nq;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "fa_types.hpp"
+
 namespace fa {
 
 struct FwdArgs {
@@ -19,6 +21,7 @@ struct FwdArgs {
     // of fwd_key_tile()), partial states in caller workspace, then a merge
     int num_splits = 1, keys_per_split = 0;
     float *Upart = nullptr, *Mpart = nullptr, *Lpart = nullptr;
+    Dropout drop{0u, 0u, 0u, 1.f};  // t = 0: no dropout
 };
 
 struct BwdArgs {
@@ -30,6 +33,7 @@ struct BwdArgs {
     int causal, dtype;
     float *Dvec;  // [B*H*Nq] workspace: rowsum(dO * O)
     void *stream;
+    Dropout drop{0u, 0u, 0u, 1.f};  // t = 0: no dropout
 };
 
 hipError_t launch_fwd(const FwdArgs &a);
