@@ -155,8 +155,10 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
     const void *dOh = static_cast<const char *>(dO) + q_head * (E == ELT_F32 ? 4 : 2);
     u32x4_t qreg[CH_PER_T], dreg[CH_PER_T];
     float lreg = 0.f, dvreg = 0.f;
+    int qt_next_row0 = 0;
     auto load_tile = [&](int qt, int buf) __attribute__((always_inline)) {
         const int q0 = qt * BQ;
+        qt_next_row0 = q0;
         if constexpr (DMA) {
             dma_tile<D, BQ, NW>(Qh, q0, Nq, Qs[buf], wave, lane);
             dma_tile<D, BQ, NW>(dOh, q0, Nq, dOs[buf], wave, lane);
@@ -174,11 +176,9 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
                 }
             }
         }
-        if (tid < BQ) {
-            const int qq = q0 + tid;
-            lreg = qq < Nq ? LSE[(int64_t)bh * Nq + qq] * kLog2e : INFINITY;  // P = 0 on padding rows
-            dvreg = qq < Nq ? Dvec[(int64_t)bh * Nq + qq] : 0.f;
-        }
+        const int qq = min(q0 + (tid & (BQ - 1)), Nq - 1);
+        lreg = LSE[(int64_t)bh * Nq + qq];
+        dvreg = Dvec[(int64_t)bh * Nq + qq];
     };
     auto store_tile = [&](int buf) __attribute__((always_inline)) {
         if constexpr (!DMA) {
@@ -191,8 +191,9 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
             }
         }
         if (tid < BQ) {
-            lse2[buf][tid] = lreg;
-            dvec[buf][tid] = dvreg;
+            const bool real = qt_next_row0 + tid < Nq;
+            lse2[buf][tid] = real ? lreg * kLog2e : INFINITY;  // P = 0 on padding rows
+            dvec[buf][tid] = real ? dvreg : 0.f;
         }
     };
 
@@ -329,8 +330,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
     constexpr int CH = BC * NCH;        // 16-byte chunks per K (and V) tile
     constexpr int CH_PER_T = DMA ? 1 : (CH + NT - 1) / NT;
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * D];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BC * D];
+    // One __shared__ object per buffer (see the dK/dV pass): the transposed reads of
+    // K must be distinguishable from the copies filling the other buffers.
+    __shared__ __attribute__((aligned(16))) uint16_t Ks0[BC * D], Ks1[BC * D], Vs0[BC * D], Vs1[BC * D];
+    auto kbuf = [&](int b) __attribute__((always_inline)) { return b ? Ks1 : Ks0; };
+    auto vbuf = [&](int b) __attribute__((always_inline)) { return b ? Vs1 : Vs0; };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, g = lane >> 5;
@@ -371,8 +375,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
     u32x4_t kreg[CH_PER_T], vreg[CH_PER_T];
     auto load_tile = [&](int k0, int buf) __attribute__((always_inline)) {
         if constexpr (DMA) {
-            dma_tile<D, BC, NW>(Kh, k0, Nk, Ks[buf], wave, lane);
-            dma_tile<D, BC, NW>(Vh, k0, Nk, Vs[buf], wave, lane);
+            dma_tile<D, BC, NW>(Kh, k0, Nk, kbuf(buf), wave, lane);
+            dma_tile<D, BC, NW>(Vh, k0, Nk, vbuf(buf), wave, lane);
         } else {
 #pragma unroll
             for (int j = 0; j < CH_PER_T; ++j) {
@@ -394,8 +398,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
                 const int i = tid + j * NT;
                 const int row = i / NCH, c = i % NCH;
                 if (i < CH) {
-                    *reinterpret_cast<u32x4_t *>(&Ks[buf][tile_off<D>(row, c * 8)]) = kreg[j];
-                    *reinterpret_cast<u32x4_t *>(&Vs[buf][tile_off<D>(row, c * 8)]) = vreg[j];
+                    *reinterpret_cast<u32x4_t *>(&kbuf(buf)[tile_off<D>(row, c * 8)]) = kreg[j];
+                    *reinterpret_cast<u32x4_t *>(&vbuf(buf)[tile_off<D>(row, c * 8)]) = vreg[j];
                 }
             }
         }
@@ -417,36 +421,31 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
         if (more) load_tile(k0 + BC, buf ^ 1);
 
         if (!CAUSAL || k0 <= q_wave0 + 31) {
-            // S^T = K Q^T and dP^T = V dO^T: lane = query, register r -> key k0 + 32kb + 8*(r/4) + 4*g + r%4
-            f32x16_t s[NKB], dp[NKB];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) { s[kb] = f32x16_t{}; dp[kb] = f32x16_t{}; }
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    const int off = tile_off<D>(kb * 32 + l32, 16 * ks + 8 * g);
-                    s[kb] = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&Ks[buf][off]), qf[ks], s[kb]);
-                    dp[kb] = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&Vs[buf][off]), df[ks], dp[kb]);
-                }
-            // masked scores -> -inf (P = 0), in a branch of its own taken only on the
-            // ragged or diagonal tile
             const bool ragged = k0 + BC > Nk;
             const bool diag = CAUSAL && (k0 + BC - 1 > q_wave0);
-            if (ragged || diag) {
-                keep_branch();
+            // One 32-key block at a time (S, dP and dS of 32 keys live at once,
+            // which keeps the kernel within 256 VGPRs without spills).
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
+            for (int kb = 0; kb < NKB; ++kb) {
+                // S^T = K Q^T and dP^T = V dO^T: lane = query, register r -> key k0 + 32kb + 8*(r/4) + 4*g + r%4
+                f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int off = tile_off<D>(kb * 32 + l32, 16 * ks + 8 * g);
+                    s = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&kbuf(buf)[off]), qf[ks], s);
+                    dp = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&vbuf(buf)[off]), df[ks], dp);
+                }
+                // masked scores -> -inf (P = 0), in a branch of its own taken only on the
+                // ragged or diagonal tile
+                if (ragged || diag) {
+                    keep_branch();
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * g + (r % 4);
-                        if (key >= Nk || (CAUSAL && key > q)) s[kb][r] = -INFINITY;
+                        if (key >= Nk || (CAUSAL && key > q)) s[r] = -INFINITY;
                     }
-            }
-            uint32_t dd[NKB][8];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                uint32_t keep = 0xffffu;  // bit r: register r of this block survives dropout
+                }
+                uint32_t keep = 0xffffu;  // bit r: register r survives dropout
                 if constexpr (DROP) {
                     keep = 0;
 #pragma unroll
@@ -454,29 +453,30 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
                         keep |= dropout_keep_keys(dr, (uint32_t)bh, (uint32_t)q, (uint32_t)(k0 + 32 * kb + 8 * rq + 4 * g))
                                 << (4 * rq);
                 }
+                uint32_t dd[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     float t[2];
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
                         const int r = 2 * i + e;
-                        const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -lse2));
+                        const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -lse2));
                         if constexpr (DROP)
-                            t[e] = pv * (((keep >> r) & 1u ? dp[kb][r] * dr.keep_scale : 0.f) - dv);
+                            t[e] = pv * (((keep >> r) & 1u ? dp[r] * dr.keep_scale : 0.f) - dv);
                         else
-                            t[e] = pv * (dp[kb][r] - dv);
+                            t[e] = pv * (dp[r] - dv);
                     }
-                    dd[kb][i] = pack_in<E>(t[0], t[1]);
+                    dd[i] = pack_in<E>(t[0], t[1]);
                 }
-            }
-            // dQ^T += K^T dS^T; k-step kst covers keys k0 + 16kst .. k0 + 16kst + 15
+                // dQ^T += K^T dS^T; k-step kst covers keys k0 + 16kst .. k0 + 16kst + 15
 #pragma unroll
-            for (int kst = 0; kst < BC / 16; ++kst) {
-                const int kb = kst / 2, h = kst % 2;
-                const u32x4_t b = {dd[kb][4 * h], dd[kb][4 * h + 1], dd[kb][4 * h + 2], dd[kb][4 * h + 3]};
+                for (int h = 0; h < 2; ++h) {
+                    const int kst = 2 * kb + h;
+                    const u32x4_t b = {dd[4 * h], dd[4 * h + 1], dd[4 * h + 2], dd[4 * h + 3]};
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    dqT[db] = mfma_in<E>(tr_operand<D>(Ks[buf], 16 * kst, 32 * db, lane), b, dqT[db]);
+                    for (int db = 0; db < NDB; ++db)
+                        dqT[db] = mfma_in<E>(tr_operand<D>(kbuf(buf), 16 * kst, 32 * db, lane), b, dqT[db]);
+                }
             }
         }
         if (more) store_tile(buf ^ 1);
