@@ -173,8 +173,10 @@ def test_workload_train_fwd():
 
 
 def test_workload_long_causal():
+    """B1 H32 N65536 d128 causal at full size: 256 seeded query rows of every
+    head against the oracle (rows 0, 1 and N-1 always among them)."""
     w = synth.WORKLOADS["long_causal_n65536"]
-    _sampled_check(w, rows_per_head=256 if os.environ.get("FA_FULL_SAMPLE") else 32)
+    _sampled_check(w, rows_per_head=256)
 
 
 def test_deterministic():

@@ -228,64 +228,6 @@ __device__ __forceinline__ void dma_tile(const void *g, int row0, int nrows, uin
     }
 }
 
-// ---- buffer-resource loads.  A resource describes [base, base + bytes);
-// lanes whose byte offset falls at or past the end read zeros (the hardware
-// range check), so a ragged tile needs no guarded path.  Offsets are 32-bit
-// byte offsets from the base; the scalar offset is always 0 so that the range
-// check sees the whole offset.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int kBufferDword3 = 0x00020000;  // untyped 32-bit data format
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferDword3);
-}
-__device__ __forceinline__ u32x2_t buf_load8(rsrc_t r, uint32_t voff) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
-}
-__device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, uint32_t voff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
-}
-
-// Per-lane part of a dma_tile copy that does not change from tile to tile:
-// which rows this lane fills in the blocks its wave copies, and the element
-// offset (row and swizzled chunk) of its 16-byte source piece.  A tile copy is
-// then one 64-bit add and one global_load_lds per block.  (global_load_lds
-// rather than the buffer form: the compiler does not track its LDS write, so
-// it adds no wait on the prefetch before later LDS reads; the explicit
-// wait_vmem() before the barrier that publishes the tile covers it.)
-template <int W, int R, int NWAVES>
-struct DmaPlan {
-    static constexpr int RPB = 512 / W;  // rows per 1 KiB block
-    static constexpr int NBLK = R / RPB;
-    static constexpr int PER = (NBLK + NWAVES - 1) / NWAVES;
-    static_assert(R % RPB == 0, "tile rows must fill whole 1 KiB blocks");
-    int row[PER];
-    uint32_t off[PER];
-    __device__ __forceinline__ DmaPlan(int wave, int lane) {
-        const int r_in = lane / (W / 8), p = lane % (W / 8);
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int b = wave + i * NWAVES;
-            row[i] = b * RPB + r_in;
-            off[i] = (uint32_t)(row[i] * W + ((p ^ swz<W>(row[i])) << 3));
-        }
-    }
-    // Copy rows [0, R) of the tile starting at `tile` (wave-uniform pointer);
-    // rows at or past `rows_valid` re-read row rows_valid - 1 (finite data that
-    // the caller gives zero weight).  `wave` must be wave-uniform.
-    __device__ __forceinline__ void issue(const uint16_t *tile, int rows_valid, uint16_t *lds, int wave) const {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int b = wave + i * NWAVES;
-            if (NBLK % NWAVES == 0 || b < NBLK) {
-                uint32_t o = off[i];
-                if (rows_valid < R && row[i] >= rows_valid) o -= (uint32_t)((row[i] - rows_valid + 1) * W);
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(tile + o),
-                                                 (__attribute__((address_space(3))) void *)(lds + b * 512), 16, 0, 0);
-            }
-        }
-    }
-};
-
 // ---- attention dropout (inverted dropout on P, the mask drawn again in the
 // backward).  The generator is Philox4x32 with 10 rounds from Salmon, Moraes,
 // Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC 2011):
