@@ -232,12 +232,13 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
             }
             // P = exp2(s*c - LSE*log2e), dS = P (dP - D)
             uint32_t pp[8], dd[8];
+            uint32_t keep16 = 0xffffu;  // dropout keep flags: bit 4rq + i, query q0 + 8rq + 4g + i
+            if constexpr (DROP) keep16 = dropout_keep_key_lane(dr, (uint32_t)bh, (uint32_t)(q0 + 4 * g), (uint32_t)kw, lane);
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
                 const f32x4_t L4 = *reinterpret_cast<const f32x4_t *>(&lse2[buf][qh * 32 + 8 * rq + 4 * g]);
                 const f32x4_t D4 = *reinterpret_cast<const f32x4_t *>(&dvec[buf][qh * 32 + 8 * rq + 4 * g]);
-                uint32_t keep = 0xfu;  // bit i: query q0 + 8rq + 4g + i survives dropout for this key
-                if constexpr (DROP) keep = dropout_keep_queries(dr, (uint32_t)bh, (uint32_t)(q0 + 8 * rq + 4 * g), (uint32_t)kw);
+                const uint32_t keep = (keep16 >> (4 * rq)) & 0xfu;  // bit i: query q0 + 8rq + 4g + i kept
                 float p[4], t[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -446,13 +447,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
                     }
                 }
                 uint32_t keep = 0xffffu;  // bit r: register r survives dropout
-                if constexpr (DROP) {
-                    keep = 0;
-#pragma unroll
-                    for (int rq = 0; rq < 4; ++rq)
-                        keep |= dropout_keep_keys(dr, (uint32_t)bh, (uint32_t)q, (uint32_t)(k0 + 32 * kb + 8 * rq + 4 * g))
-                                << (4 * rq);
-                }
+                if constexpr (DROP)
+                    keep = dropout_keep_query_lane(dr, (uint32_t)bh, (uint32_t)q, (uint32_t)(k0 + 32 * kb + 4 * g), lane);
                 uint32_t dd[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {

@@ -256,25 +256,66 @@ __device__ __forceinline__ u32x4_t philox4x32_10(uint32_t c0, uint32_t c1, uint3
     return u32x4_t{c0, c1, c2, c3};
 }
 
-// Keep flags (bit e set = keep) of keys j4 .. j4+3 for query i (j4 % 4 == 0).
-__device__ __forceinline__ uint32_t dropout_keep_keys(const Dropout &dr, uint32_t bh, uint32_t i, uint32_t j4) {
-    const u32x4_t w = philox4x32_10(j4 >> 2, i >> 2, bh, 0u, dr.k0, dr.k1);
-    const uint32_t s = i & 3u;
-    const uint32_t word = s == 0 ? w[0] : s == 1 ? w[1] : s == 2 ? w[2] : w[3];
-    uint32_t keep = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) keep |= (((word >> (8 * e)) & 0xffu) >= dr.t ? 1u : 0u) << e;
+// Bit e set: byte e of w is below t, i.e. that element is dropped.  Bytes 0/2
+// and 1/3 go through a packed 16-bit subtraction; the sign bit of byte - t is
+// set exactly when byte < t (both in 0..255).  t2 = t | t << 16.
+__device__ __forceinline__ uint32_t dropped_bytes(uint32_t w, uint32_t t2) {
+    typedef short s16x2_t __attribute__((ext_vector_type(2)));
+    const uint32_t dl = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2_t, w & 0x00ff00ffu) -
+                                                         __builtin_bit_cast(s16x2_t, t2));
+    const uint32_t dh = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2_t, (w >> 8) & 0x00ff00ffu) -
+                                                         __builtin_bit_cast(s16x2_t, t2));
+    return ((dl >> 15) & 1u) | ((dh >> 14) & 2u) | ((dl >> 29) & 4u) | ((dh >> 28) & 8u);
+}
+
+// x from lane (this lane ^ s) of the same quad (s = 1, 2, 3; DPP quad permutation).
+template <int S>
+__device__ __forceinline__ uint32_t quad_xor(uint32_t x) {
+    constexpr int ctrl = S == 1 ? 0xB1 : S == 2 ? 0x4E : 0x1B;  // [1,0,3,2] [2,3,0,1] [3,2,1,0]
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, ctrl, 0xF, 0xF, false);
+}
+
+// The four lanes of a quad hold four consecutive queries (or keys) and need the
+// same four generator calls of a 16-query x 4-key (or 4-query x 16-key) strip;
+// lane w evaluates call w alone and the keep flags travel through three quad
+// exchanges.  `packed` holds, for each of the quad's lanes w', a nibble at bits
+// 4w' .. 4w'+3; the result gathers nibble (this lane) of lane (this lane ^ s)
+// into bits 4(this lane ^ s) .. +3.
+__device__ __forceinline__ uint32_t quad_gather_nibbles(uint32_t packed, uint32_t w) {
+    const uint32_t sh = 4u * w;
+    uint32_t keep = ((packed >> sh) & 0xfu) << sh;
+    keep |= ((quad_xor<1>(packed) >> sh) & 0xfu) << (4u * (w ^ 1u));
+    keep |= ((quad_xor<2>(packed) >> sh) & 0xfu) << (4u * (w ^ 2u));
+    keep |= ((quad_xor<3>(packed) >> sh) & 0xfu) << (4u * (w ^ 3u));
     return keep;
 }
 
-// Keep flags (bit e set = keep) of queries i4 .. i4+3 for key j (i4 % 4 == 0).
-__device__ __forceinline__ uint32_t dropout_keep_queries(const Dropout &dr, uint32_t bh, uint32_t i4, uint32_t j) {
-    const u32x4_t w = philox4x32_10(j >> 2, i4 >> 2, bh, 0u, dr.k0, dr.k1);
-    const uint32_t sh = 8u * (j & 3u);
-    uint32_t keep = 0;
+// Keep flags of a lane that owns query q (q % 4 == lane % 4) for the 16 keys
+// kbase + 8 rq + e (rq, e = 0..3; kbase % 4 == 0): bit 4 rq + e.
+__device__ __forceinline__ uint32_t dropout_keep_query_lane(const Dropout &dr, uint32_t bh, uint32_t q, uint32_t kbase,
+                                                            int lane) {
+    const uint32_t w = (uint32_t)lane & 3u, t2 = dr.t | (dr.t << 16);
+    const u32x4_t out = philox4x32_10((kbase + 8u * w) >> 2, q >> 2, bh, 0u, dr.k0, dr.k1);  // key group rq = w
+    uint32_t packed = 0;  // nibble i: keep flags of the group's 4 keys for query 4(q/4) + i
 #pragma unroll
-    for (int e = 0; e < 4; ++e) keep |= (((w[e] >> sh) & 0xffu) >= dr.t ? 1u : 0u) << e;
-    return keep;
+    for (int i = 0; i < 4; ++i) packed |= (~dropped_bytes(out[i], t2) & 0xfu) << (4 * i);
+    return quad_gather_nibbles(packed, w);
+}
+
+// Keep flags of a lane that owns key j (j % 4 == lane % 4) for the 16 queries
+// qbase + 8 rq + i (rq, i = 0..3; qbase % 4 == 0): bit 4 rq + i.
+__device__ __forceinline__ uint32_t dropout_keep_key_lane(const Dropout &dr, uint32_t bh, uint32_t qbase, uint32_t j,
+                                                          int lane) {
+    const uint32_t w = (uint32_t)lane & 3u, t2 = dr.t | (dr.t << 16);
+    const u32x4_t out = philox4x32_10(j >> 2, (qbase + 8u * w) >> 2, bh, 0u, dr.k0, dr.k1);  // query group rq = w
+    uint32_t packed = 0;  // nibble e: keep flags of the group's 4 queries for key 4(j/4) + e
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t kept = ~dropped_bytes(out[i], t2);  // bit e: key e kept for query i
+#pragma unroll
+        for (int e = 0; e < 4; ++e) packed |= ((kept >> e) & 1u) << (4 * e + i);
+    }
+    return quad_gather_nibbles(packed, w);
 }
 
 // Map a hardware workgroup index to a logical one so that consecutive

@@ -36,8 +36,9 @@
 //
 // Dropout (DROP = true): the row sum l takes the undropped P (the softmax is
 // not changed), the P V product takes P with the dropped elements zeroed,
-// and the epilogue multiplies by 1 / (1 - rate) together with 1 / l.  Each
-// lane draws the keep flags of its own query row, four keys per Philox call.
+// and the epilogue multiplies by 1 / (1 - rate) together with 1 / l.  The
+// four lanes of a quad (four consecutive query rows) share the generator calls
+// of each 32-key block (fa_common.hpp, dropout_keep_query_lane).
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -300,12 +301,8 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 uint32_t keep = 0;  // bit r: register r of this block survives dropout
-                if constexpr (DROP) {
-#pragma unroll
-                    for (int rq = 0; rq < 4; ++rq)
-                        keep |= dropout_keep_keys(dr, (uint32_t)bh, (uint32_t)q, (uint32_t)(k0 + 32 * kb + 8 * rq + 4 * g))
-                                << (4 * rq);
-                }
+                if constexpr (DROP)
+                    keep = dropout_keep_query_lane(dr, (uint32_t)bh, (uint32_t)q, (uint32_t)(k0 + 32 * kb + 4 * g), lane);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i], scale_log2, -m_used));
