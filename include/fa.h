@@ -103,8 +103,8 @@ fa_status fa_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, f
 /*
  * A split count for fa_fwd_splitkv on one MI355X (256 CUs): 1 when fa_fwd
  * already launches a workgroup per CU, otherwise enough ranges for about one
- * workgroup per CU, keeping at least eight 64-key tiles per range.  Returns
- * 0 for invalid sizes.
+ * workgroup per CU, keeping at least 512 keys per range.  Returns 0 for
+ * invalid sizes.
  */
 int fa_fwd_num_splits(int B, int H, int Nq, int Nk, int d, int causal);
 

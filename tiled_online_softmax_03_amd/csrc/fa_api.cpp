@@ -92,7 +92,7 @@ fa_status fa_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, f
     if (st != FA_OK) return st;
     const size_t need = fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, num_splits);
     if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
-    const int BQ = fa::fwd_query_tile(), BC = fa::fwd_key_tile();
+    const int BQ = fa::fwd_query_tile(), BC = fa::fwd_key_tile(d);
     const int64_t grid = (int64_t)B * H * ((Nq + BQ - 1) / BQ) * num_splits;
     if (grid >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
     const size_t rows = (size_t)B * H * Nq * (size_t)num_splits;
@@ -118,14 +118,15 @@ int fa_fwd_num_splits(int B, int H, int Nq, int Nk, int d, int causal) {
     // against 8192 keys; 32 heads of 128 queries against 32768 keys): the
     // best count gives about one workgroup per CU and keeps 8 or more key
     // tiles per range; beyond that the extra prologues and the merge cost more
-    // than the added parallelism gains.
-    constexpr int kCUs = 256, kMinTilesPerSplit = 8;
-    const int BQ = fa::fwd_query_tile(), BC = fa::fwd_key_tile();
+    // than the added parallelism gains.  (512 keys = 8 tiles of 64 at d = 128, 4 of
+    // 128 at d = 64.)
+    constexpr int kCUs = 256, kMinKeysPerSplit = 512;
+    const int BQ = fa::fwd_query_tile(), BC = fa::fwd_key_tile(d);
     const int64_t wgs = (int64_t)B * H * ((Nq + BQ - 1) / BQ);
     if (wgs >= kCUs) return 1;
     const int n_kt = (Nk + BC - 1) / BC;
     int64_t g = (kCUs + wgs - 1) / wgs;
-    const int64_t g_max = n_kt / kMinTilesPerSplit;
+    const int64_t g_max = (int64_t)n_kt * BC / kMinKeysPerSplit;
     if (g > g_max) g = g_max;
     if (g > FA_MAX_SPLITS) g = FA_MAX_SPLITS;
     return g < 1 ? 1 : (int)g;

@@ -382,6 +382,14 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
 #ifndef FA_FWD_KEYS
 #define FA_FWD_KEYS 64
 #endif
+// Keys per tile: at d = 64 each tile carries half the matrix work of d = 128, so
+// it takes twice as many keys to keep the per-tile costs (barrier, staging) the
+// same fraction of the time.
+#ifndef FA_FWD_KEYS_D64
+#define FA_FWD_KEYS_D64 128
+#endif
+template <int D>
+constexpr int fwd_keys() { return D == 64 ? FA_FWD_KEYS_D64 : FA_FWD_KEYS; }
 
 // Merge of the split-KV partial states: one thread per 4 columns of a row.
 template <int D, int E>
@@ -413,7 +421,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(SplitOut part, int G, in
 
 template <int D, int E, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs &a) {
-    constexpr int BC = FA_FWD_KEYS, NW = FA_FWD_WAVES, BR = 32 * NW;
+    constexpr int BC = fwd_keys<D>(), NW = FA_FWD_WAVES, BR = 32 * NW;
     const int n_qt = (a.Nq + BR - 1) / BR;
     const int BH = a.B * a.H;
     const dim3 block(NW * 64);
@@ -458,12 +466,12 @@ static hipError_t launch_fwd_d(const FwdArgs &a) {
 
 hipError_t launch_fwd(const FwdArgs &a) { return a.d == 64 ? launch_fwd_d<64>(a) : launch_fwd_d<128>(a); }
 
-int fwd_key_tile() { return FA_FWD_KEYS; }
+int fwd_key_tile(int d) { return d == 64 ? fwd_keys<64>() : fwd_keys<128>(); }
 int fwd_query_tile() { return 32 * FA_FWD_WAVES; }
 
 const char *describe_fwd() {
-    return "fwd_kernel<D, BC=64, waves=8 (256 query rows, 32 per wave), double-buffered K/V^T in LDS, "
-           "S^T=KQ^T bf16/f16 MFMA 32x32x16, PV fp16 MFMA, lazy rescale>";
+    return "fwd_kernel<D, keys per tile 64 (d=128) / 128 (d=64), waves=8 (256 query rows, 32 per wave), "
+           "double-buffered K/V^T in LDS, S^T=KQ^T bf16/f16 MFMA 32x32x16, PV fp16 MFMA, lazy rescale>";
 }
 
 }  // namespace fa

@@ -18,7 +18,7 @@ struct FwdArgs {
     int causal, dtype;
     void *stream;
     // split-KV: num_splits > 1 key ranges of keys_per_split keys (a multiple
-    // of fwd_key_tile()), partial states in caller workspace, then a merge
+    // of fwd_key_tile(d)), partial states in caller workspace, then a merge
     int num_splits = 1, keys_per_split = 0;
     float *Upart = nullptr, *Mpart = nullptr, *Lpart = nullptr;
     Dropout drop{0u, 0u, 0u, 1.f};  // t = 0: no dropout
@@ -37,7 +37,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs &a);
-int fwd_key_tile();    // keys per tile of the forward's key loop
+int fwd_key_tile(int d);  // keys per tile of the forward's key loop for head dim d
 int fwd_query_tile();  // query rows per forward workgroup
 constexpr int kBwdStages = 3;
 // stage < 0 runs every stage in order.
