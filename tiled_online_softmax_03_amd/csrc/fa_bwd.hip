@@ -496,7 +496,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
     }
 }
 
-constexpr int kDqKeys = 64;  // keys per tile of the dQ pass
+// Keys per tile of the dQ pass: at d = 64 a tile carries half the matrix work
+// of d = 128, so it takes twice the keys (the 32-key blocks inside keep the
+// registers the same).
+template <int D, int E>
+constexpr int dq_keys() { return E == ELT_F32 ? 32 : D == 64 ? 128 : 64; }
 template <int D, int E, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
     hipStream_t st = (hipStream_t)a.stream;
@@ -524,7 +528,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
     }
     if (stage < 0 || stage == 2) {
         const int n_qt = (a.Nq + 255) / 256;
-        constexpr int BC = E == ELT_F32 ? 32 : kDqKeys;
+        constexpr int BC = dq_keys<D, E>();
         if (drop)
             hipLaunchKernelGGL((bwd_dq_kernel<D, BC, E, CAUSAL, true>), dim3(BH * n_qt), dim3(512), 0, st, a.Q, a.K, a.V,
                                a.dO, a.LSE, a.Dvec, a.dQ, BH, a.Nq, a.Nk, a.scale, sl2, n_qt, a.drop);
@@ -558,7 +562,7 @@ hipError_t launch_bwd(const BwdArgs &a, int stage) {
 const char *describe_bwd() {
     return "bwd_pre_kernel (D=rowsum(dO*O)) -> bwd_dkdv_kernel<D, 8 waves = 4 key groups x 2 query halves, "
            "128 keys, 64-row query steps, "
-           "double-buffered Q/dO, transposed LDS reads> -> bwd_dq_kernel<D, 8 waves x 32 rows, 64-key tiles>; "
+           "double-buffered Q/dO, transposed LDS reads> -> bwd_dq_kernel<D, 8 waves x 32 rows, 64-key tiles (128 at d=64)>; "
            "no atomics";
 }
 
