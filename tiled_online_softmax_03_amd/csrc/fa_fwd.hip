@@ -49,11 +49,46 @@ namespace fa {
 // V^T tile in LDS: [D][BC] fp16.  Each row holds, per 16-key group kst, two
 // 16-byte chunks: chunk 2*kst + g carries keys 16kst + 4g + 0..3 and
 // 16kst + 8 + 4g + 0..3, exactly the eight k-slots lane group g feeds to the
-// PV matrix product, so one ds_read_b128 fetches a whole operand.  Chunks are
-// XOR-swizzled per row so that eight consecutive rows read at one chunk hit
-// distinct banks.
+// PV matrix product, so one ds_read_b128 fetches a whole operand.
+//
+// Placement (64 banks of 4 bytes): row `col` is stored at vt_row(col) with its
+// chunks XORed by vt_xor(col), chosen so that both access shapes are free of
+// bank conflicts:
+//  * operand reads: 16 lanes read 16 consecutive rows at one chunk;
+//  * the transposed stores (vblock below): 32 lanes write 8 bytes each into
+//    16 rows four apart, at two chunk halves.
+// With 64 keys a row is 128 bytes (half the banks): (row parity, chunk) must
+// be a bijection both on col bits 0..3 (reads) and on bits 2..5 (stores);
+// parity = bit 0 ^ bit 4, chunk xor = bits 1..3 ^ bit 5 does both.  With 128
+// keys a row spans all banks and the chunk alone must be distinct.
 template <int BC>
-__device__ __forceinline__ int vtswz(int col) { return (col + col / (BC / 8)) % (BC / 8); }
+__device__ __forceinline__ int vt_row(int col) {
+    if constexpr (BC == 64) return col ^ ((col >> 4) & 1);
+    return col;
+}
+template <int BC>
+__device__ __forceinline__ int vt_xor(int col) {
+    if constexpr (BC == 64) return ((col >> 1) & 7) ^ ((col >> 5) & 1);
+    return (col + col / (BC / 8)) % (BC / 8);
+}
+
+// Thread -> (key quad u, column quad c4) of the V staging: each 32-lane half
+// of a wave covers 16 consecutive column quads of two key quads two apart (the
+// two chunk halves), which the V^T layout above stores without bank
+// conflicts; each 16-lane group still reads a contiguous row segment.
+template <int D, int BC>
+__device__ __forceinline__ void vblock(int tid, int &c4, int &u) {
+    static_assert((BC / 4) * (D / 4) == 512 && (D == 128 || D == 64), "one V block per thread of 8 waves");
+    const int w = tid >> 6, l = tid & 63;
+    const int c4lo = l & 15, h = (l >> 4) & 1, hi = l >> 5;
+    if constexpr (D == 128) {
+        c4 = c4lo + 16 * hi;
+        u = 4 * (w >> 1) + 2 * h + (w & 1);
+    } else {
+        c4 = c4lo;
+        u = 4 * w + 2 * h + hi;
+    }
+}
 
 // Rescale threshold (log2 units): the running maximum used for the
 // exponentials is only moved when a new score exceeds it by more than this,
@@ -168,7 +203,8 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
 #pragma unroll
             for (int j = 0; j < VBLK_PER_T; ++j) {
                 const int i = tid + j * NT;
-                const int c4 = i % (D / 4), u = i / (D / 4);  // keys 4u..4u+3, columns 4c4..4c4+3
+                int c4, u;  // keys 4u..4u+3, columns 4c4..4c4+3
+                vblock<D, BC>(i, c4, u);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int key = k0 + 4 * u + k;
@@ -202,7 +238,8 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
 #pragma unroll
         for (int j = 0; j < VBLK_PER_T; ++j) {
             const int i = tid + j * NT;
-            const int c4 = i % (D / 4), u = i / (D / 4);
+            int c4, u;
+            vblock<D, BC>(i, c4, u);
             if (i < VBLK) {
                 float v[4][4];  // [key][column]
 #pragma unroll
@@ -225,7 +262,7 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int col = 4 * c4 + e;
-                    *reinterpret_cast<u32x2_t *>(&Vt[buf][col * BC + ((chunk ^ vtswz<BC>(col)) * 8) + half * 4]) =
+                    *reinterpret_cast<u32x2_t *>(&Vt[buf][vt_row<BC>(col) * BC + ((chunk ^ vt_xor<BC>(col)) * 8) + half * 4]) =
                         u32x2_t{pack_f16(v[0][e], v[1][e]), pack_f16(v[2][e], v[3][e])};
                 }
             }
@@ -326,7 +363,7 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
                 for (int db = 0; db < NDB; ++db) {
                     const int col = db * 32 + l32;
                     const u32x4_t a = *reinterpret_cast<const u32x4_t *>(
-                        &Vt[buf][col * BC + (((2 * kst + g) ^ vtswz<BC>(col)) * 8)]);
+                        &Vt[buf][vt_row<BC>(col) * BC + (((2 * kst + g) ^ vt_xor<BC>(col)) * 8)]);
                     o[db] = mfma_f16(a, b, o[db]);
                 }
             }
