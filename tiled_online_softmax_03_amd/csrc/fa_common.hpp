@@ -117,24 +117,6 @@ __device__ __forceinline__ void load8_float(const void *base, int64_t elem, floa
     }
 }
 
-// Four consecutive elements of an E-typed row as floats (fp32 rounded to
-// bf16 first, as everywhere else).
-template <int E>
-__device__ __forceinline__ void load4_float(const void *base, int64_t elem, float out[4]) {
-    if constexpr (E == ELT_F32) {
-        const f32x4_t a = *reinterpret_cast<const f32x4_t *>(static_cast<const float *>(base) + elem);
-        const uint32_t w0 = pack_bf16(a[0], a[1]), w1 = pack_bf16(a[2], a[3]);
-        out[0] = bf16_lo(w0); out[1] = bf16_hi(w0); out[2] = bf16_lo(w1); out[3] = bf16_hi(w1);
-    } else {
-        const u32x2_t w = *reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(base) + elem);
-        if constexpr (E == ELT_BF16) {
-            out[0] = bf16_lo(w[0]); out[1] = bf16_hi(w[0]); out[2] = bf16_lo(w[1]); out[3] = bf16_hi(w[1]);
-        } else {
-            out[0] = f16_lo(w[0]); out[1] = f16_hi(w[0]); out[2] = f16_lo(w[1]); out[3] = f16_hi(w[1]);
-        }
-    }
-}
-
 // Store four consecutive floats to an E-typed row (RNE for 16-bit types).
 template <int E>
 __device__ __forceinline__ void store4(void *base, int64_t elem, float a, float b, float c, float d) {
