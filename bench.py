@@ -168,7 +168,7 @@ def main():
         "bwd_pre_kernel": ("hbm", 2 * rows * w.d * elt + rows * 4),  # read O, dO; write D
         "bwd_dkdv_kernel": ("mfma", 2.0 * F),         # S, dP, dV, dK
         "bwd_dq_kernel": ("mfma", 1.5 * F),           # S, dP, dQ
-        "fa_bwd_dropout (3 kernels)": ("mfma", 2.5 * F),  # the whole backward, spec convention
+        "fa_bwd_dropout (3 kernels)": ("mfma", 2.5 * F),  # the whole backward, 2.5 F by the metric's convention
     }
     dom = max(names, key=lambda n: kern_ms[n])
     bound, units = work[dom]
