@@ -1,0 +1,53 @@
+"""The largest inputs the ABI accepts: B*H*max(Nq, Nk)*d just below 2^31
+elements (4 GiB per 16-bit tensor), so element offsets of the last heads
+pass 2^31 bytes.  Forward and backward run at that size; the oracle checks
+whole heads at the start, middle and end of the batch (heads are
+independent, so each is checked exactly)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import tiled_online_softmax_03_amd as fa
+from gpu_util import check_forward, check_grads, oracle_view, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.lib()
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_max_elements(d):
+    N = 1024
+    H = (1 << 31) // (N * d) - 1  # the largest head count below the 2^31-element limit
+    B = 1
+    assert B * H * N * d < (1 << 31) and (B * H + 1) * N * d >= (1 << 31)
+    say("limits", (B, H, N, N, d), "bf16")
+    inp = synth.make_inputs(B, H, N, N, d, "bf16", 31 + d, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    O, LSE = fa.forward(inp["Q"], inp["K"], inp["V"], scale)
+    dQ, dK, dV = fa.backward(inp["Q"], inp["K"], inp["V"], O, inp["dO"], LSE, scale)
+    torch.cuda.synchronize()
+    heads = [0, H // 2, H - 1]
+    pick = lambda t: t.reshape(H, 1, t.shape[2], t.shape[3])[heads]
+    q, k, v, do = (oracle_view(pick(inp[n])) for n in ("Q", "K", "V", "dO"))
+    rdQ, rdK, rdV, rO, rL = oracle.bwd(q, k, v, do, scale)
+    A_ref, _ = oracle.fwd(q, k, np.abs(v), scale)
+    check_forward(to_np(pick(O)), to_np(LSE.reshape(H, 1, N)[heads]), rO, rL, torch.bfloat16, "limits", A_ref, N,
+                  float(np.abs(v).max()))
+    check_grads({"dQ": to_np(pick(dQ)), "dK": to_np(pick(dK)), "dV": to_np(pick(dV))},
+                {"dQ": rdQ, "dK": rdK, "dV": rdV}, "limits")
+    # one more head would cross the limit: refused before any launch
+    one = torch.empty((1, 1, N, d), device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty((1, 1, N), device="cuda", dtype=torch.float32)
+    st = fa.lib().fa_fwd(one.data_ptr(), one.data_ptr(), one.data_ptr(), one.data_ptr(), lse.data_ptr(), B, H + 1, N,
+                         N, d, scale, 0, fa.FA_BF16, None)
+    assert st == fa.FA_ERR_UNSUPPORTED
