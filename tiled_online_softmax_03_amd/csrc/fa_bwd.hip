@@ -37,6 +37,11 @@
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
+// Query rows per step of the dK/dV pass at d = 64 (64 at d = 128).
+#ifndef FA_DKDV_ROWS_D64
+#define FA_DKDV_ROWS_D64 128
+#endif
+
 namespace fa {
 
 // Floats of eight consecutive stored elements, without rounding fp32 data.
@@ -89,7 +94,13 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
     constexpr int NW = 8, NT = 512;
     constexpr int NKG = 4;        // key groups
     constexpr int BKC = 32 * NKG; // keys per workgroup
-    constexpr int BQ = 64;        // query rows per step (32 per query half)
+    // Query rows per step: at d = 64 every product carries half the work of
+    // d = 128, so a step takes twice the rows (each wave walks its half in
+    // 32-row blocks) to keep the barrier, the staging and the exponentials the
+    // same share of the time.
+    constexpr int BQ = D == 64 ? FA_DKDV_ROWS_D64 : 64;
+    constexpr int QH = BQ / 2;    // rows of one query half in a step
+    static_assert(QH % 32 == 0, "query halves are whole 32-row blocks");
     constexpr int NCH = D / 8;    // 16-byte chunks per row
     constexpr int NKS = D / 16;   // k-steps over the head dim
     constexpr int NDB = D / 32;   // 32-row blocks of dK^T / dV^T
@@ -216,58 +227,123 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
         if (more) load_tile(qt + 1, buf ^ 1);  // in flight during this step's math
         const uint16_t *qs = Qs[buf];
         const uint16_t *ds = dOs[buf];
-        const int q0 = qt * BQ + qh * 32;
+        // (The d = 128 branch keeps a single block in this exact form: the compiler's
+        // schedule of the d = 128 kernel was measured 7 % slower when it was
+        // written as the one-iteration case of the loop below.)
+        if constexpr (QH == 32) {
+            const int q0 = qt * BQ + qh * 32;
 
-        if (!CAUSAL || q0 + 31 >= kw0) {  // else every row of the block precedes this wave's keys
-            // S = Q K^T and dP = dO V^T: lane = key, register r -> query q0 + 8*(r/4) + 4*g + r%4
-            f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+            if (!CAUSAL || q0 + 31 >= kw0) {  // else every row of the block precedes this wave's keys
+                // S = Q K^T and dP = dO V^T: lane = key, register r -> query q0 + 8*(r/4) + 4*g + r%4
+                f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const int qoff = tile_off<D>(qh * 32 + l32, 16 * ks + 8 * g);
-                const int koff = tile_off<D>(kg * 32 + l32, 16 * ks + 8 * g);
-                s = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&qs[qoff]),
-                               *reinterpret_cast<const u32x4_t *>(&Ks[koff]), s);
-                dp = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&ds[qoff]),
-                                *reinterpret_cast<const u32x4_t *>(&Vs[koff]), dp);
-            }
-            // P = exp2(s*c - LSE*log2e), dS = P (dP - D)
-            uint32_t pp[8], dd[8];
-            uint32_t keep16 = 0xffffu;  // dropout keep flags: bit 4rq + i, query q0 + 8rq + 4g + i
-            if constexpr (DROP) keep16 = dropout_keep_key_lane(dr, (uint32_t)bh, (uint32_t)(q0 + 4 * g), (uint32_t)kw, lane);
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int qoff = tile_off<D>(qh * 32 + l32, 16 * ks + 8 * g);
+                    const int koff = tile_off<D>(kg * 32 + l32, 16 * ks + 8 * g);
+                    s = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&qs[qoff]),
+                                   *reinterpret_cast<const u32x4_t *>(&Ks[koff]), s);
+                    dp = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&ds[qoff]),
+                                    *reinterpret_cast<const u32x4_t *>(&Vs[koff]), dp);
+                }
+                // P = exp2(s*c - LSE*log2e), dS = P (dP - D)
+                uint32_t pp[8], dd[8];
+                uint32_t keep16 = 0xffffu;  // dropout keep flags: bit 4rq + i, query q0 + 8rq + 4g + i
+                if constexpr (DROP) keep16 = dropout_keep_key_lane(dr, (uint32_t)bh, (uint32_t)(q0 + 4 * g), (uint32_t)kw, lane);
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const f32x4_t L4 = *reinterpret_cast<const f32x4_t *>(&lse2[buf][qh * 32 + 8 * rq + 4 * g]);
-                const f32x4_t D4 = *reinterpret_cast<const f32x4_t *>(&dvec[buf][qh * 32 + 8 * rq + 4 * g]);
-                const uint32_t keep = (keep16 >> (4 * rq)) & 0xfu;  // bit i: query q0 + 8rq + 4g + i kept
-                float p[4], t[4];
+                for (int rq = 0; rq < 4; ++rq) {
+                    const f32x4_t L4 = *reinterpret_cast<const f32x4_t *>(&lse2[buf][qh * 32 + 8 * rq + 4 * g]);
+                    const f32x4_t D4 = *reinterpret_cast<const f32x4_t *>(&dvec[buf][qh * 32 + 8 * rq + 4 * g]);
+                    const uint32_t keep = (keep16 >> (4 * rq)) & 0xfu;  // bit i: query q0 + 8rq + 4g + i kept
+                    float p[4], t[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * rq + i;
-                    float pv = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -L4[i]));
-                    if (CAUSAL && kw > q0 + 8 * rq + 4 * g + i) pv = 0.f;
-                    if constexpr (DROP) {
-                        const bool kept = (keep >> i) & 1u;
-                        p[i] = kept ? pv * dr.keep_scale : 0.f;
-                        t[i] = pv * ((kept ? dp[r] * dr.keep_scale : 0.f) - D4[i]);
-                    } else {
-                        p[i] = pv;
-                        t[i] = pv * (dp[r] - D4[i]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 4 * rq + i;
+                        float pv = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -L4[i]));
+                        if (CAUSAL && kw > q0 + 8 * rq + 4 * g + i) pv = 0.f;
+                        if constexpr (DROP) {
+                            const bool kept = (keep >> i) & 1u;
+                            p[i] = kept ? pv * dr.keep_scale : 0.f;
+                            t[i] = pv * ((kept ? dp[r] * dr.keep_scale : 0.f) - D4[i]);
+                        } else {
+                            p[i] = pv;
+                            t[i] = pv * (dp[r] - D4[i]);
+                        }
+                    }
+                    pp[2 * rq] = pack_in<E>(p[0], p[1]);
+                    pp[2 * rq + 1] = pack_in<E>(p[2], p[3]);
+                    dd[2 * rq] = pack_in<E>(t[0], t[1]);
+                    dd[2 * rq + 1] = pack_in<E>(t[2], t[3]);
+                }
+                // dV^T += dO^T P and dK^T += Q^T dS; k-step h covers query rows 16h..16h+15 of the block
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const u32x4_t bp = {pp[4 * h], pp[4 * h + 1], pp[4 * h + 2], pp[4 * h + 3]};
+                    const u32x4_t bs = {dd[4 * h], dd[4 * h + 1], dd[4 * h + 2], dd[4 * h + 3]};
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        dvT[db] = mfma_in<E>(tr_operand<D>(ds, qh * 32 + 16 * h, 32 * db, lane), bp, dvT[db]);
+                        dkT[db] = mfma_in<E>(tr_operand<D>(qs, qh * 32 + 16 * h, 32 * db, lane), bs, dkT[db]);
                     }
                 }
-                pp[2 * rq] = pack_in<E>(p[0], p[1]);
-                pp[2 * rq + 1] = pack_in<E>(p[2], p[3]);
-                dd[2 * rq] = pack_in<E>(t[0], t[1]);
-                dd[2 * rq + 1] = pack_in<E>(t[2], t[3]);
             }
-            // dV^T += dO^T P and dK^T += Q^T dS; k-step h covers query rows 16h..16h+15 of the block
+        } else {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const u32x4_t bp = {pp[4 * h], pp[4 * h + 1], pp[4 * h + 2], pp[4 * h + 3]};
-                const u32x4_t bs = {dd[4 * h], dd[4 * h + 1], dd[4 * h + 2], dd[4 * h + 3]};
+            for (int sub = 0; sub < QH / 32; ++sub) {
+                const int r0 = qh * QH + 32 * sub;  // first row of this 32-row block in the tile
+                const int q0 = qt * BQ + r0;
+
+                if (!CAUSAL || q0 + 31 >= kw0) {  // else every row of the block precedes this wave's keys
+                    // S = Q K^T and dP = dO V^T: lane = key, register r -> query q0 + 8*(r/4) + 4*g + r%4
+                    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    dvT[db] = mfma_in<E>(tr_operand<D>(ds, qh * 32 + 16 * h, 32 * db, lane), bp, dvT[db]);
-                    dkT[db] = mfma_in<E>(tr_operand<D>(qs, qh * 32 + 16 * h, 32 * db, lane), bs, dkT[db]);
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const int qoff = tile_off<D>(r0 + l32, 16 * ks + 8 * g);
+                        const int koff = tile_off<D>(kg * 32 + l32, 16 * ks + 8 * g);
+                        s = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&qs[qoff]),
+                                       *reinterpret_cast<const u32x4_t *>(&Ks[koff]), s);
+                        dp = mfma_in<E>(*reinterpret_cast<const u32x4_t *>(&ds[qoff]),
+                                        *reinterpret_cast<const u32x4_t *>(&Vs[koff]), dp);
+                    }
+                    // P = exp2(s*c - LSE*log2e), dS = P (dP - D)
+                    uint32_t pp[8], dd[8];
+                    uint32_t keep16 = 0xffffu;  // dropout keep flags: bit 4rq + i, query q0 + 8rq + 4g + i
+                    if constexpr (DROP) keep16 = dropout_keep_key_lane(dr, (uint32_t)bh, (uint32_t)(q0 + 4 * g), (uint32_t)kw, lane);
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const f32x4_t L4 = *reinterpret_cast<const f32x4_t *>(&lse2[buf][r0 + 8 * rq + 4 * g]);
+                        const f32x4_t D4 = *reinterpret_cast<const f32x4_t *>(&dvec[buf][r0 + 8 * rq + 4 * g]);
+                        const uint32_t keep = (keep16 >> (4 * rq)) & 0xfu;  // bit i: query q0 + 8rq + 4g + i kept
+                        float p[4], t[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = 4 * rq + i;
+                            float pv = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -L4[i]));
+                            if (CAUSAL && kw > q0 + 8 * rq + 4 * g + i) pv = 0.f;
+                            if constexpr (DROP) {
+                                const bool kept = (keep >> i) & 1u;
+                                p[i] = kept ? pv * dr.keep_scale : 0.f;
+                                t[i] = pv * ((kept ? dp[r] * dr.keep_scale : 0.f) - D4[i]);
+                            } else {
+                                p[i] = pv;
+                                t[i] = pv * (dp[r] - D4[i]);
+                            }
+                        }
+                        pp[2 * rq] = pack_in<E>(p[0], p[1]);
+                        pp[2 * rq + 1] = pack_in<E>(p[2], p[3]);
+                        dd[2 * rq] = pack_in<E>(t[0], t[1]);
+                        dd[2 * rq + 1] = pack_in<E>(t[2], t[3]);
+                    }
+                    // dV^T += dO^T P and dK^T += Q^T dS; k-step h covers query rows 16h..16h+15 of the block
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const u32x4_t bp = {pp[4 * h], pp[4 * h + 1], pp[4 * h + 2], pp[4 * h + 3]};
+                        const u32x4_t bs = {dd[4 * h], dd[4 * h + 1], dd[4 * h + 2], dd[4 * h + 3]};
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db) {
+                            dvT[db] = mfma_in<E>(tr_operand<D>(ds, r0 + 16 * h, 32 * db, lane), bp, dvT[db]);
+                            dkT[db] = mfma_in<E>(tr_operand<D>(qs, r0 + 16 * h, 32 * db, lane), bs, dkT[db]);
+                        }
+                    }
                 }
             }
         }
