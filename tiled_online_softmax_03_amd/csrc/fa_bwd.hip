@@ -637,7 +637,7 @@ hipError_t launch_bwd(const BwdArgs &a, int stage) {
 
 const char *describe_bwd() {
     return "bwd_pre_kernel (D=rowsum(dO*O)) -> bwd_dkdv_kernel<D, 8 waves = 4 key groups x 2 query halves, "
-           "128 keys, 64-row query steps, "
+           "128 keys, 64-row query steps (128 at d=64), "
            "double-buffered Q/dO, transposed LDS reads> -> bwd_dq_kernel<D, 8 waves x 32 rows, 64-key tiles (128 at d=64)>; "
            "no atomics";
 }
