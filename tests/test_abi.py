@@ -27,7 +27,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
     assert names == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_num_stages", "fa_bwd_stage", "fa_bwd_workspace_size",
                      "fa_describe", "fa_dropout_threshold", "fa_fwd", "fa_fwd_dropout", "fa_fwd_num_splits",
-                     "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_status_string"]
+                     "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_workspace_size", "fa_fwd_ws",
+                     "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -106,6 +107,32 @@ def _bwd(lib, ws=P, ws_bytes=1 << 40, dQ=P, d=64, dtype=0, Nq=8):
 ])
 def test_bwd_rejects(lib, kw, status):
     assert _bwd(lib, **kw) == status
+
+
+def test_fwd_workspace_size(lib):
+    # fp16 V^T tiles of 64 keys (d = 128) or 128 keys (d = 64), the last one padded
+    pad = lambda n: (n + 255) // 256 * 256
+    assert fa.fa_fwd_workspace_size(2, 3, 100, 130, 128) == pad(2 * 3 * 3 * 64 * 128 * 2)
+    assert fa.fa_fwd_workspace_size(2, 3, 100, 130, 64) == pad(2 * 3 * 2 * 128 * 64 * 2)
+    assert fa.fa_fwd_workspace_size(1, 1, 1, 1, 64) == 128 * 64 * 2
+    assert fa.fa_fwd_workspace_size(0, 3, 100, 130, 64) == 0
+    assert fa.fa_fwd_workspace_size(2, 3, 100, 130, 96) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=NULL), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=ctypes.c_void_p(0x10010)), fa.FA_ERR_INVALID_ARG),  # not 256-byte aligned
+    (dict(ws_bytes=128 * 64 * 2 - 1), fa.FA_ERR_INVALID_ARG),
+    (dict(Q=MIS), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=5), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fwd_ws_rejects(lib, kw, status):
+    a = dict(Q=P, ws=P, ws_bytes=1 << 40, Nk=8, d=64, dtype=0)
+    a.update(kw)
+    assert lib.fa_fwd_ws(a["Q"], P, P, P, P, 1, 1, 8, a["Nk"], a["d"], 0.125, 0, a["dtype"], a["ws"], a["ws_bytes"],
+                         NULL) == status
 
 
 def test_binding_refuses_cpu_tensors():

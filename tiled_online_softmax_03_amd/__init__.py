@@ -8,6 +8,8 @@ raises.
 Entry points keep the C names:
 
     fa_fwd(Q, K, V, O, LSE, scale, causal=False, stream=None)
+    fa_fwd_ws(Q, K, V, O, LSE, workspace, scale, causal=False, stream=None)
+    fa_fwd_workspace_size(B, H, Nq, Nk, d) -> int
     fa_fwd_splitkv(Q, K, V, O, LSE, num_splits, workspace, scale, causal=False, stream=None)
     fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, num_splits) -> int
     fa_fwd_num_splits(B, H, Nq, Nk, d, causal) -> int
@@ -56,6 +58,10 @@ def lib() -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     L.fa_fwd.restype = i
+    L.fa_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    L.fa_fwd_ws.restype = i
+    L.fa_fwd_workspace_size.argtypes = [i, i, i, i, i]
+    L.fa_fwd_workspace_size.restype = sz
     L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     L.fa_fwd_splitkv.restype = i
     L.fa_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i, i]
@@ -129,6 +135,26 @@ def fa_fwd(Q, K, V, O, LSE, scale=None, causal=False, stream=None) -> None:
                       int(bool(causal)), dtype_code(Q.dtype), _stream_handle(stream))
     if st != FA_OK:
         raise FaError(st, "fa_fwd")
+
+
+def fa_fwd_workspace_size(B, H, Nq, Nk, d) -> int:
+    return int(lib().fa_fwd_workspace_size(B, H, Nq, Nk, d))
+
+
+def fa_fwd_ws(Q, K, V, O, LSE, workspace, scale=None, causal=False, stream=None) -> None:
+    B, H, Nq, Nk, d = _dims(Q, K)
+    for t in (Q, K, V, O, LSE, workspace):
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    _need(K.shape == V.shape and O.shape == Q.shape and tuple(LSE.shape) == (B, H, Nq), "shape mismatch")
+    _need(Q.dtype == K.dtype == V.dtype == O.dtype, "Q, K, V, O must share a dtype")
+    _need(str(LSE.dtype) == "torch.float32", "LSE must be float32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib().fa_fwd_ws(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, H, Nq, Nk, d, float(scale),
+                         int(bool(causal)), dtype_code(Q.dtype), _ptr(workspace), nbytes, _stream_handle(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_ws")
 
 
 def fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, num_splits) -> int:

@@ -64,6 +64,26 @@ fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LS
     return fwd_impl(Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, causal, dtype, make_dropout(0, 0), stream);
 }
 
+size_t fa_fwd_workspace_size(int B, int H, int Nq, int Nk, int d) {
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return 0;
+    return pad256(fa::fwd_packed_v_bytes(B, H, Nk, d));
+}
+
+fa_status fa_fwd_ws(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H, int Nq, int Nk,
+                    int d, float scale, int causal, int dtype, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    if (!Q || !K || !V || !O || !LSE || !workspace) return FA_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+        return FA_ERR_INVALID_ARG;
+    if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_INVALID_ARG;
+    const fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (workspace_bytes < fa_fwd_workspace_size(B, H, Nq, Nk, d)) return FA_ERR_INVALID_ARG;
+    fa::FwdArgs a{Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, causal ? 1 : 0, dtype, stream};
+    a.Vpk = static_cast<uint16_t *>(workspace);
+    return fa::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_fwd_dropout(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H, int Nq,
                          int Nk, int d, float scale, int causal, int dtype, float dropout_p, unsigned long long seed,
                          void *stream) {

@@ -90,6 +90,56 @@ __device__ __forceinline__ void vblock(int tid, int &c4, int &u) {
     }
 }
 
+// V^T tiles prepared once per call for fa_fwd_ws: tile (bh, kt) of BC keys is
+// written to Vpk exactly as the key loop keeps it in LDS (fp16, [D][BC],
+// vt_row / vt_xor placement, zero past Nk), so the loop copies it global ->
+// LDS with no conversion or transposition of its own.  One workgroup per
+// tile: the same per-thread 4-key x 4-column blocks as the in-loop staging,
+// written transposed into LDS, then copied out 16 bytes per lane.
+template <int D, int BC, int E>
+__global__ __launch_bounds__(512) void v_pack_kernel(const void *__restrict__ V, uint16_t *__restrict__ Vpk, int Nk,
+                                                     int n_kt) {
+    static_assert((BC / 4) * (D / 4) == 512 && D * BC * 2 == 16 * 1024, "one block per thread, 16 KiB tiles");
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * BC];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x / n_kt, k0 = (blockIdx.x % n_kt) * BC;
+    const int64_t k_head = (int64_t)bh * Nk * D;
+    int c4, u;  // keys k0 + 4u .. +3, columns 4c4 .. 4c4+3
+    vblock<D, BC>(tid, c4, u);
+    float v[4][4];  // [key][column], in the operand precision
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int key = k0 + 4 * u + k;
+        if constexpr (E == ELT_F32) {
+            f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+            if (key < Nk) x = *reinterpret_cast<const f32x4_t *>(static_cast<const float *>(V) + k_head + (int64_t)key * D + 4 * c4);
+            const uint32_t w0 = pack_bf16(x[0], x[1]), w1 = pack_bf16(x[2], x[3]);  // fp32 operands are bf16
+            v[k][0] = bf16_lo(w0); v[k][1] = bf16_hi(w0); v[k][2] = bf16_lo(w1); v[k][3] = bf16_hi(w1);
+        } else {
+            u32x2_t w = {0u, 0u};
+            if (key < Nk) w = *reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(V) + k_head + (int64_t)key * D + 4 * c4);
+            if constexpr (E == ELT_BF16) {
+                v[k][0] = bf16_lo(w[0]); v[k][1] = bf16_hi(w[0]); v[k][2] = bf16_lo(w[1]); v[k][3] = bf16_hi(w[1]);
+            } else {
+                v[k][0] = f16_lo(w[0]); v[k][1] = f16_hi(w[0]); v[k][2] = f16_lo(w[1]); v[k][3] = f16_hi(w[1]);
+            }
+        }
+    }
+    const int kst = u / 4, qd = u % 4;
+    const int chunk = 2 * kst + (qd & 1), half = qd >> 1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int col = 4 * c4 + e;
+        *reinterpret_cast<u32x2_t *>(&Vt[vt_row<BC>(col) * BC + ((chunk ^ vt_xor<BC>(col)) * 8) + half * 4]) =
+            u32x2_t{pack_f16(v[0][e], v[1][e]), pack_f16(v[2][e], v[3][e])};
+    }
+    __syncthreads();
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(Vpk + (int64_t)blockIdx.x * (D * BC));
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(Vt);
+    dst[tid] = src[tid];
+    dst[tid + 512] = src[tid + 512];
+}
+
 // Rescale threshold (log2 units): the running maximum used for the
 // exponentials is only moved when a new score exceeds it by more than this,
 // so p = exp2(s*c - m_used) stays below 2^8 (far inside fp16 range) and the
@@ -113,13 +163,15 @@ struct SplitOut {
     int keys_per_split;  // a multiple of the key tile
 };
 
-template <int D, int BC, int NW, int E, bool CAUSAL, bool SPLIT, bool DROP>
+template <int D, int BC, int NW, int E, bool CAUSAL, bool SPLIT, bool DROP, bool PREV = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
                                                       const void *__restrict__ V, void *__restrict__ O,
                                                       float *__restrict__ LSE, int BH, int Nq, int Nk,
-                                                      float scale_log2, int n_qt, SplitOut part, Dropout dr) {
+                                                      float scale_log2, int n_qt, SplitOut part, Dropout dr,
+                                                      const uint16_t *__restrict__ Vpk) {
     static_assert(!(SPLIT && DROP), "split-KV has no dropout variant");
+    static_assert(!PREV || (!SPLIT && !DROP), "packed V^T tiles serve the plain forward");
     constexpr int BR = 32 * NW;    // query rows per workgroup
     constexpr int NT = NW * 64;    // threads
     constexpr int NCH = D / 8;     // 16-byte chunks per K row
@@ -196,6 +248,15 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
                 if (i < BC * NCH && k0 + row < Nk) kreg[j] = load8_operand<E>(K, k_head + (int64_t)(k0 + row) * D + c * 8);
             }
         }
+        if constexpr (PREV) {
+            // the packed V^T tile: 16 KiB copied as is, 1 KiB per wave instruction
+            const uint16_t *src = Vpk + ((int64_t)bh * ((Nk + BC - 1) / BC) + k0 / BC) * (D * BC);
+#pragma unroll
+            for (int b = wave; b < D * BC / 512; b += NW)
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + b * 512 + lane * 8),
+                                                 (__attribute__((address_space(3))) void *)(&Vt[buf][b * 512]), 16, 0, 0);
+            return;
+        }
         // Interior tiles (every key exists) take an unguarded path: a uniform branch
         // instead of one exec-masked load per key.
         auto load_v = [&](auto guarded_c) __attribute__((always_inline)) {
@@ -235,6 +296,7 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
                 if (i < BC * NCH) *reinterpret_cast<u32x4_t *>(&Ks[buf][tile_off<D>(row, c * 8)]) = kreg[j];
             }
         }
+        if constexpr (PREV) return;  // V^T arrived by copy
 #pragma unroll
         for (int j = 0; j < VBLK_PER_T; ++j) {
             const int i = tid + j * NT;
@@ -466,18 +528,28 @@ static hipError_t launch_fwd_t(const FwdArgs &a) {
     hipStream_t st = (hipStream_t)a.stream;
     if (a.drop.t > 0) {
         hipLaunchKernelGGL((fwd_kernel<D, BC, NW, E, CAUSAL, false, true>), dim3(BH * n_qt), block, 0, st, a.Q, a.K,
-                           a.V, a.O, a.LSE, BH, a.Nq, a.Nk, sl2, n_qt, SplitOut{}, a.drop);
+                           a.V, a.O, a.LSE, BH, a.Nq, a.Nk, sl2, n_qt, SplitOut{}, a.drop, nullptr);
+        return hipGetLastError();
+    }
+    if (a.num_splits <= 1 && a.Vpk) {
+        // V^T tiles packed once, then copied as they are by the key loop
+        const int n_kt = (a.Nk + BC - 1) / BC;
+        hipLaunchKernelGGL((v_pack_kernel<D, BC, E>), dim3(BH * n_kt), dim3(512), 0, st, a.V, a.Vpk, a.Nk, n_kt);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((fwd_kernel<D, BC, NW, E, CAUSAL, false, false, true>), dim3(BH * n_qt), block, 0, st, a.Q,
+                           a.K, a.V, a.O, a.LSE, BH, a.Nq, a.Nk, sl2, n_qt, SplitOut{}, Dropout{}, a.Vpk);
         return hipGetLastError();
     }
     if (a.num_splits <= 1) {
         hipLaunchKernelGGL((fwd_kernel<D, BC, NW, E, CAUSAL, false, false>), dim3(BH * n_qt), block, 0, st, a.Q, a.K,
-                           a.V, a.O, a.LSE, BH, a.Nq, a.Nk, sl2, n_qt, SplitOut{}, Dropout{});
+                           a.V, a.O, a.LSE, BH, a.Nq, a.Nk, sl2, n_qt, SplitOut{}, Dropout{}, nullptr);
         return hipGetLastError();
     }
     const int G = a.num_splits;
     const SplitOut part{a.Upart, a.Mpart, a.Lpart, a.keys_per_split};
     hipLaunchKernelGGL((fwd_kernel<D, BC, NW, E, CAUSAL, true, false>), dim3(BH * n_qt * G), block, 0, st, a.Q, a.K,
-                       a.V, a.O, a.LSE, BH, a.Nq, a.Nk, sl2, n_qt, part, Dropout{});
+                       a.V, a.O, a.LSE, BH, a.Nq, a.Nk, sl2, n_qt, part, Dropout{}, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t R = (int64_t)BH * a.Nq;
@@ -505,10 +577,15 @@ hipError_t launch_fwd(const FwdArgs &a) { return a.d == 64 ? launch_fwd_d<64>(a)
 
 int fwd_key_tile(int d) { return d == 64 ? fwd_keys<64>() : fwd_keys<128>(); }
 int fwd_query_tile() { return 32 * FA_FWD_WAVES; }
+size_t fwd_packed_v_bytes(int B, int H, int Nk, int d) {
+    const int BC = fwd_key_tile(d);
+    return (size_t)B * H * ((Nk + BC - 1) / BC) * (size_t)BC * d * 2;
+}
 
 const char *describe_fwd() {
     return "fwd_kernel<D, keys per tile 64 (d=128) / 128 (d=64), waves=8 (256 query rows, 32 per wave), "
-           "double-buffered K/V^T in LDS, S^T=KQ^T bf16/f16 MFMA 32x32x16, PV fp16 MFMA, lazy rescale>";
+           "double-buffered K/V^T in LDS, S^T=KQ^T bf16/f16 MFMA 32x32x16, PV fp16 MFMA, lazy rescale>; "
+           "fa_fwd_ws: v_pack_kernel (V -> fp16 V^T tiles in the LDS layout), then the key loop copies them";
 }
 
 }  // namespace fa

@@ -22,6 +22,9 @@ struct FwdArgs {
     int num_splits = 1, keys_per_split = 0;
     float *Upart = nullptr, *Mpart = nullptr, *Lpart = nullptr;
     Dropout drop{0u, 0u, 0u, 1.f};  // t = 0: no dropout
+    // fp16 V^T tiles in the key loop's LDS layout (fwd_packed_v_bytes), or
+    // nullptr: the key loop converts and transposes V itself
+    uint16_t *Vpk = nullptr;
 };
 
 struct BwdArgs {
@@ -39,6 +42,7 @@ struct BwdArgs {
 hipError_t launch_fwd(const FwdArgs &a);
 int fwd_key_tile(int d);  // keys per tile of the forward's key loop for head dim d
 int fwd_query_tile();  // query rows per forward workgroup
+size_t fwd_packed_v_bytes(int B, int H, int Nk, int d);  // bytes of the packed V^T tiles
 constexpr int kBwdStages = 3;
 // stage < 0 runs every stage in order.
 hipError_t launch_bwd(const BwdArgs &a, int stage);
