@@ -299,13 +299,12 @@ def sample_sclk(launch_step, seconds=4.0):
 
 def versions(torch):
     import platform
-    import subprocess
+
+    import tiled_online_softmax_03_amd as fa
     v = {"torch": torch.__version__, "hip_runtime": torch.version.hip, "python": platform.python_version()}
-    try:
-        r = subprocess.run(["hipcc", "--version"], capture_output=True, text=True, timeout=60)
-        v["hipcc"] = " | ".join(l for l in r.stdout.splitlines() if l.startswith(("HIP version", "AMD clang")))
-    except Exception:
-        v["hipcc"] = None
+    # the compiler that built libfa, from the library itself (no child process: under a
+    # profiler a child would initialise the GPU before it could exec anything)
+    v["libfa_build"] = fa.fa_build_info()
     try:
         with open("/opt/rocm/.info/version") as f:
             v["rocm"] = f.read().strip()
@@ -414,7 +413,9 @@ def kernel_source_sha256() -> str:
     import glob
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "tiled_online_softmax_03_amd", "csrc", "*"))):
+    # the kernels' sources only (the host-side ABI code does not change what a kernel moves)
+    csrc = os.path.join(ROOT, "tiled_online_softmax_03_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

@@ -197,6 +197,10 @@ fa_status fa_bwd_stage(int stage, const void *Q, const void *K, const void *V, c
                        int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* Static string naming the HIP and compiler versions the library was built
+ * with and its target, for measurement records. */
+const char *fa_build_info(void);
+
 /* Static, human-readable name of a status code ("FA_OK", ...). */
 const char *fa_status_string(int status);
 

@@ -25,12 +25,17 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert names == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_num_stages", "fa_bwd_stage", "fa_bwd_workspace_size",
+    assert names == ["fa_build_info", "fa_bwd", "fa_bwd_dropout", "fa_bwd_num_stages", "fa_bwd_stage", "fa_bwd_workspace_size",
                      "fa_describe", "fa_dropout_threshold", "fa_fwd", "fa_fwd_dropout", "fa_fwd_num_splits",
                      "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_workspace_size", "fa_fwd_ws",
                      "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_build_info(lib):
+    s = fa.fa_build_info()
+    assert s.startswith("HIP ") and "clang" in s and "gfx950" in s
 
 
 def test_status_strings(lib):

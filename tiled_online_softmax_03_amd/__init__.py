@@ -21,6 +21,7 @@ Entry points keep the C names:
     fa_bwd_num_stages() -> int
     fa_bwd_stage(stage, <fa_bwd arguments>)
     fa_status_string(status) -> str
+    fa_build_info() -> str
     fa_describe(d, dtype, causal) -> str
 
 plus ``forward`` / ``backward`` helpers that allocate the outputs.
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_workspace_size.restype = sz
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     L.fa_bwd.restype = i
+    L.fa_build_info.argtypes = []
+    L.fa_build_info.restype = ctypes.c_char_p
     L.fa_bwd_num_stages.argtypes = []
     L.fa_bwd_num_stages.restype = i
     L.fa_bwd_stage.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
@@ -255,6 +258,10 @@ def fa_bwd_stage(stage, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale=None, 
                                                    stream))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_stage")
+
+
+def fa_build_info() -> str:
+    return lib().fa_build_info().decode()
 
 
 def fa_status_string(status: int) -> str:

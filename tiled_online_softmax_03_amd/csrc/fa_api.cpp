@@ -203,6 +203,13 @@ fa_status fa_bwd_stage(int stage, const void *Q, const void *K, const void *V, c
                     workspace_bytes, stream);
 }
 
+#define FA_STR2(x) #x
+#define FA_STR(x) FA_STR2(x)
+const char *fa_build_info(void) {
+    return "HIP " FA_STR(HIP_VERSION_MAJOR) "." FA_STR(HIP_VERSION_MINOR) "." FA_STR(HIP_VERSION_PATCH)
+           ", clang " __clang_version__ ", offload arch gfx950";
+}
+
 const char *fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "FA_OK";
