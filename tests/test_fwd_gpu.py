@@ -132,11 +132,23 @@ def test_workload_single_head_fwd():
     _full_check(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.causal, w.seed, w.sigma_qk, w.name)
 
 
-def _sampled_check(w, rows_per_head, heads=None, label=""):
+def _run_fwd_ws(inp, scale, causal):
+    """fa_fwd_ws (V packed once into the workspace), the forward bench.py times for Nq >= 2048."""
+    Q, K = inp["Q"], inp["K"]
+    B, H, Nq, d = Q.shape
+    ws = torch.empty(fa.fa_fwd_workspace_size(B, H, Nq, K.shape[2], d), device="cuda", dtype=torch.uint8)
+    O = torch.empty_like(Q)
+    LSE = torch.empty((B, H, Nq), device="cuda", dtype=torch.float32)
+    fa.fa_fwd_ws(Q, K, inp["V"], O, LSE, ws, scale, causal)
+    torch.cuda.synchronize()
+    return O, LSE
+
+
+def _sampled_check(w, rows_per_head, heads=None, label="", run=_run_fwd):
     """Full-size launch; the oracle evaluates sampled query rows one by one."""
     inp = synth.workload_inputs(w, device="cuda", with_dO=False)
     say("fwd", label or w.name, "full size", (w.B, w.H, w.Nq, w.Nk, w.d))
-    O, LSE = _run_fwd(inp, w.scale, w.causal)
+    O, LSE = run(inp, w.scale, w.causal)
     BH = w.B * w.H
     heads = list(range(BH)) if heads is None else heads
     rows = synth.sample_rows(w.Nq, BH, rows_per_head)
@@ -177,6 +189,15 @@ def test_workload_long_causal():
     head against the oracle (rows 0, 1 and N-1 always among them)."""
     w = synth.WORKLOADS["long_causal_n65536"]
     _sampled_check(w, rows_per_head=256)
+
+
+@pytest.mark.parametrize("name,rows,step", [("long_causal_n65536", 256, 1), ("train_b8h32n4096d128", 16, 3),
+                                            ("single_head_fwd", 256, 1)])
+def test_workload_fwd_ws(name, rows, step):
+    """The same full-size checks through fa_fwd_ws, the launch bench.py times for these workloads."""
+    w = synth.WORKLOADS[name]
+    _sampled_check(w, rows_per_head=rows, heads=list(range(0, w.B * w.H, step)), label=w.name + " fa_fwd_ws",
+                   run=_run_fwd_ws)
 
 
 def test_deterministic():
