@@ -352,6 +352,13 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
         const bool more = kt + 1 < n_kt;
         if (more) load_tile(k0 + BC, buf ^ 1);  // in flight during this tile's math
         if (!CAUSAL || k0 <= q_wave0 + 31) {  // else the tile lies above the diagonal for every row of this wave
+            // dropout keep flags first: they do not depend on the scores, so the
+            // generator's vector work can run beside the S^T products
+            uint32_t keepv[NKB];  // bit r: register r of block kb survives dropout
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                keepv[kb] = DROP ? dropout_keep_query_lane(dr, (uint32_t)bh, (uint32_t)q,
+                                                           (uint32_t)(k0 + 32 * kb + 4 * g), lane) : 0u;
             // ---- S^T = K Q^T : lane = query, register r -> key 8*(r/4) + 4*g + r%4 of each 32-key block
             f32x16_t s[NKB];
 #pragma unroll
@@ -399,9 +406,7 @@ void fwd_kernel(const void *__restrict__ Q, const void *__restrict__ K,
             uint32_t pk[NKB][8];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                uint32_t keep = 0;  // bit r: register r of this block survives dropout
-                if constexpr (DROP)
-                    keep = dropout_keep_query_lane(dr, (uint32_t)bh, (uint32_t)q, (uint32_t)(k0 + 32 * kb + 4 * g), lane);
+                const uint32_t keep = keepv[kb];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i], scale_log2, -m_used));
