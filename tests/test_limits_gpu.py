@@ -1,6 +1,6 @@
 """The largest inputs the ABI accepts: B*H*max(Nq, Nk)*d just below 2^31
 elements (4 GiB per 16-bit tensor), so element offsets of the last heads
-pass 2^31 bytes.  Forward and backward run at that size; the oracle checks
+pass 2^31 bytes.  Forward (fa_fwd and fa_fwd_ws) and backward run at that size; the oracle checks
 whole heads at the start, middle and end of the batch (heads are
 independent, so each is checked exactly)."""
 import math
@@ -45,6 +45,13 @@ def test_max_elements(d):
                   float(np.abs(v).max()))
     check_grads({"dQ": to_np(pick(dQ)), "dK": to_np(pick(dK)), "dV": to_np(pick(dV))},
                 {"dQ": rdQ, "dK": rdK, "dV": rdV}, "limits")
+    # the packed-V forward at the same size (its workspace tiles also pass 2^31 bytes): same bits
+    ws = torch.empty(fa.fa_fwd_workspace_size(B, H, N, N, d), device="cuda", dtype=torch.uint8)
+    O2, L2 = torch.empty_like(O), torch.empty_like(LSE)
+    fa.fa_fwd_ws(inp["Q"], inp["K"], inp["V"], O2, L2, ws, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(O2, O) and torch.equal(L2, LSE)
+    del ws, O2, L2
     # one more head would cross the limit: refused before any launch
     one = torch.empty((1, 1, N, d), device="cuda", dtype=torch.bfloat16)
     lse = torch.empty((1, 1, N), device="cuda", dtype=torch.float32)
