@@ -4,6 +4,7 @@ the pins constrain every part of the oracle (scale, sign, index, mask,
 normalisation, recurrence), not just that the oracle passes them."""
 import os
 
+import numpy as np
 import pytest
 
 import oracle
@@ -60,7 +61,8 @@ def test_mutant_is_caught(tmp_path, name, old, new):
     failed = []
     for pin in pins.ALL_PINS:
         try:
-            pin(o)
+            with np.errstate(divide="raise", invalid="raise"):  # a NaN or division by zero is a catch too
+                pin(o)
         except (AssertionError, FloatingPointError, RuntimeError, ValueError, ZeroDivisionError):
             failed.append(pin.__name__)
     assert failed, "mutant %s passed every pin" % name
