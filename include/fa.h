@@ -53,7 +53,7 @@ extern "C" {
 typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, size <= 0, scale not finite and > 0, workspace too small */
-    FA_ERR_UNSUPPORTED = 2, /* head dim or dtype this build has no kernel for, size too large */
+    FA_ERR_UNSUPPORTED = 2, /* head dim or dtype the library has no kernel for, size too large */
     FA_ERR_HIP = 3          /* the HIP runtime rejected a launch */
 } fa_status;
 
