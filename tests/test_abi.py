@@ -47,11 +47,17 @@ def test_status_strings(lib):
 
 
 def test_describe(lib):
+    # the whole description fits: it names every kernel of a step, the last one included,
+    # and ends with the backward's closing clause (a truncated copy would not)
     for d in (64, 128):
         for dt in (0, 1, 2):
             for c in (0, 1):
                 s = fa.fa_describe(d, dt, c)
-                assert "fwd" in s and "bwd" in s and ("d=%d" % d) in s
+                assert ("d=%d" % d) in s and ("causal=%d" % c) in s
+                for k in ("fwd_kernel", "v_pack_kernel", "bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"):
+                    assert k in s, (k, s)
+                assert s.endswith("no atomics"), s
+                assert len(s) < 2047, len(s)
     assert fa.fa_describe(96, 0, 0) == "unsupported"
     assert fa.fa_describe(64, 7, 0) == "unsupported"
 
@@ -143,8 +149,57 @@ def test_fwd_ws_rejects(lib, kw, status):
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     Q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError, match="device"):
         fa.forward(Q, Q, Q)
+
+
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", ["K_batch", "K_heads", "K_dim", "V_shape", "O_shape", "LSE_shape", "LSE_dtype",
+                                  "dtype_mix"])
+def test_binding_checks_forward_shapes(case):
+    # every shape or dtype mistake is a ValueError raised before any pointer reaches the
+    # library (CPU tensors: the check must come before the device check)
+    torch = pytest.importorskip("torch")
+    B, H, Nq, Nk, d = 2, 3, 8, 5, 64
+    t = dict(Q=_t(B, H, Nq, d), K=_t(B, H, Nk, d), V=_t(B, H, Nk, d), O=_t(B, H, Nq, d),
+             LSE=_t(B, H, Nq, dtype=torch.float32))
+    bad = {"K_batch": ("K", _t(1, H, Nk, d)), "K_heads": ("K", _t(B, 1, Nk, d)), "K_dim": ("K", _t(B, H, Nk, 128)),
+           "V_shape": ("V", _t(B, H, Nk + 1, d)), "O_shape": ("O", _t(B, H, Nq - 1, d)),
+           "LSE_shape": ("LSE", _t(B, H, Nq + 1, dtype=torch.float32)), "LSE_dtype": ("LSE", _t(B, H, Nq)),
+           "dtype_mix": ("V", _t(B, H, Nk, d, dtype=torch.float16))}[case]
+    t[bad[0]] = bad[1]
+    for call in (lambda: fa.fa_fwd(t["Q"], t["K"], t["V"], t["O"], t["LSE"]),
+                 lambda: fa.fa_fwd_ws(t["Q"], t["K"], t["V"], t["O"], t["LSE"], _t(1024, dtype=torch.uint8)),
+                 lambda: fa.fa_fwd_splitkv(t["Q"], t["K"], t["V"], t["O"], t["LSE"], 2, _t(1024, dtype=torch.uint8)),
+                 lambda: fa.fa_fwd_dropout(t["Q"], t["K"], t["V"], t["O"], t["LSE"], 0.1, 7)):
+        with pytest.raises(ValueError) as e:
+            call()
+        assert "device" not in str(e.value), e.value
+
+
+@pytest.mark.parametrize("case", ["dO_shape", "dQ_shape", "dK_shape", "dV_shape", "LSE_shape", "LSE_dtype",
+                                  "K_batch", "dtype_mix"])
+def test_binding_checks_backward_shapes(case):
+    torch = pytest.importorskip("torch")
+    B, H, Nq, Nk, d = 2, 3, 8, 5, 64
+    t = dict(Q=_t(B, H, Nq, d), K=_t(B, H, Nk, d), V=_t(B, H, Nk, d), O=_t(B, H, Nq, d), dO=_t(B, H, Nq, d),
+             LSE=_t(B, H, Nq, dtype=torch.float32), dQ=_t(B, H, Nq, d), dK=_t(B, H, Nk, d), dV=_t(B, H, Nk, d))
+    bad = {"dO_shape": ("dO", _t(B, H, Nq, 128)), "dQ_shape": ("dQ", _t(B, H, Nk, d)),
+           "dK_shape": ("dK", _t(B, H, Nq, d)), "dV_shape": ("dV", _t(B, 1, Nk, d)),
+           "LSE_shape": ("LSE", _t(1, H, Nq, dtype=torch.float32)), "LSE_dtype": ("LSE", _t(B, H, Nq)),
+           "K_batch": ("K", _t(1, H, Nk, d)), "dtype_mix": ("dK", _t(B, H, Nk, d, dtype=torch.float16))}[case]
+    t[bad[0]] = bad[1]
+    ws = _t(1 << 16, dtype=torch.uint8)
+    a = [t[k] for k in ("Q", "K", "V", "O", "dO", "LSE", "dQ", "dK", "dV")]
+    for call in (lambda: fa.fa_bwd(*a, ws), lambda: fa.fa_bwd_stage(1, *a, ws),
+                 lambda: fa.fa_bwd_dropout(*a, ws, 0.1, 7)):
+        with pytest.raises(ValueError) as e:
+            call()
+        assert "device" not in str(e.value), e.value
 
 
 def test_bwd_stages(lib):
@@ -199,6 +254,10 @@ def test_num_splits(lib):
     assert fa.fa_fwd_num_splits(4, 16, 1024, 8192, 64, False) == 1
     # a single query row against 8192 keys, 8 heads: 8 workgroups -> 16 ranges (8 tiles each)
     assert fa.fa_fwd_num_splits(1, 8, 1, 8192, 128, False) == 16
+    # causal: no row sees keys past Nq - 1, so a long key sequence does not add ranges
+    assert fa.fa_fwd_num_splits(1, 8, 1, 8192, 128, True) == 1
+    assert fa.fa_fwd_num_splits(1, 1, 4096, 4096, 64, True) == 8
+    assert fa.fa_fwd_num_splits(1, 1, 1024, 8192, 128, True) == 2
     # too few keys to split
     assert fa.fa_fwd_num_splits(1, 1, 64, 100, 64, False) == 1
     assert fa.fa_fwd_num_splits(0, 1, 64, 100, 64, False) == 0

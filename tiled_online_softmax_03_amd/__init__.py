@@ -117,6 +117,8 @@ def _dims(Q, K):
     if Q.dim() != 4 or K.dim() != 4:
         raise ValueError("expected [B, H, N, d] tensors")
     B, H, Nq, d = Q.shape
+    _need(K.shape[0] == B and K.shape[1] == H and K.shape[3] == d,
+          "K must be [B, H, Nk, d] with Q's B, H and d (Q %s, K %s)" % (tuple(Q.shape), tuple(K.shape)))
     return B, H, Nq, K.shape[2], d
 
 
@@ -125,13 +127,37 @@ def _need(cond, msg):
         raise ValueError(msg)
 
 
-def fa_fwd(Q, K, V, O, LSE, scale=None, causal=False, stream=None) -> None:
+def _check(Q, K, V, O, LSE, dO=None, dQ=None, dK=None, dV=None, extra=()):
+    """Every check the C ABI cannot make on device pointers: shapes (K and V
+    [B, H, Nk, d] with Q's B, H and d; O, dO, dQ shaped like Q; dK, dV like K;
+    LSE float32 [B, H, Nq]), one shared dtype, contiguous device tensors on one
+    device.  Shapes and dtypes are checked first, so a mistake is reported
+    before anything touches a device.  Returns (B, H, Nq, Nk, d)."""
     B, H, Nq, Nk, d = _dims(Q, K)
-    for t in (Q, K, V, O, LSE):
+    _need(V.shape == K.shape, "V must have K's shape (K %s, V %s)" % (tuple(K.shape), tuple(V.shape)))
+    for name, t in (("O", O), ("dO", dO), ("dQ", dQ)):
+        if t is not None:
+            _need(t.shape == Q.shape, "%s must have Q's shape (Q %s, %s %s)" % (name, tuple(Q.shape), name,
+                                                                                tuple(t.shape)))
+    for name, t in (("dK", dK), ("dV", dV)):
+        if t is not None:
+            _need(t.shape == K.shape, "%s must have K's shape (K %s, %s %s)" % (name, tuple(K.shape), name,
+                                                                                tuple(t.shape)))
+    _need(tuple(LSE.shape) == (B, H, Nq), "LSE must be [B, H, Nq] = %s, got %s" % ((B, H, Nq), tuple(LSE.shape)))
+    _need(str(LSE.dtype) == "torch.float32", "LSE must be float32, got %s" % LSE.dtype)
+    tensors = [t for t in (Q, K, V, O, dO, dQ, dK, dV) if t is not None]
+    _need(len({t.dtype for t in tensors}) == 1, "Q, K, V, O (and dO, dQ, dK, dV) must share a dtype")
+    dtype_code(Q.dtype)
+    devs = set()
+    for t in tensors + [LSE] + [t for t in extra if t is not None]:
         _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
-    _need(K.shape == V.shape and O.shape == Q.shape and tuple(LSE.shape) == (B, H, Nq), "shape mismatch")
-    _need(Q.dtype == K.dtype == V.dtype == O.dtype, "Q, K, V, O must share a dtype")
-    _need(str(LSE.dtype) == "torch.float32", "LSE must be float32")
+        devs.add(t.device)
+    _need(len(devs) == 1, "all tensors must be on one device")
+    return B, H, Nq, Nk, d
+
+
+def fa_fwd(Q, K, V, O, LSE, scale=None, causal=False, stream=None) -> None:
+    B, H, Nq, Nk, d = _check(Q, K, V, O, LSE)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = lib().fa_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, H, Nq, Nk, d, float(scale),
@@ -145,12 +171,7 @@ def fa_fwd_workspace_size(B, H, Nq, Nk, d) -> int:
 
 
 def fa_fwd_ws(Q, K, V, O, LSE, workspace, scale=None, causal=False, stream=None) -> None:
-    B, H, Nq, Nk, d = _dims(Q, K)
-    for t in (Q, K, V, O, LSE, workspace):
-        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
-    _need(K.shape == V.shape and O.shape == Q.shape and tuple(LSE.shape) == (B, H, Nq), "shape mismatch")
-    _need(Q.dtype == K.dtype == V.dtype == O.dtype, "Q, K, V, O must share a dtype")
-    _need(str(LSE.dtype) == "torch.float32", "LSE must be float32")
+    B, H, Nq, Nk, d = _check(Q, K, V, O, LSE, extra=(workspace,))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     nbytes = workspace.numel() * workspace.element_size()
@@ -169,14 +190,7 @@ def fa_fwd_num_splits(B, H, Nq, Nk, d, causal=False) -> int:
 
 
 def fa_fwd_splitkv(Q, K, V, O, LSE, num_splits, workspace, scale=None, causal=False, stream=None) -> None:
-    B, H, Nq, Nk, d = _dims(Q, K)
-    for t in (Q, K, V, O, LSE):
-        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
-    _need(K.shape == V.shape and O.shape == Q.shape and tuple(LSE.shape) == (B, H, Nq), "shape mismatch")
-    _need(Q.dtype == K.dtype == V.dtype == O.dtype, "Q, K, V, O must share a dtype")
-    _need(str(LSE.dtype) == "torch.float32", "LSE must be float32")
-    if workspace is not None:
-        _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
+    B, H, Nq, Nk, d = _check(Q, K, V, O, LSE, extra=(workspace,))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     wptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
@@ -192,18 +206,8 @@ def fa_dropout_threshold(dropout_p) -> int:
     return int(lib().fa_dropout_threshold(float(dropout_p)))
 
 
-def _fwd_check(Q, K, V, O, LSE):
-    B, H, Nq, Nk, d = _dims(Q, K)
-    for t in (Q, K, V, O, LSE):
-        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
-    _need(K.shape == V.shape and O.shape == Q.shape and tuple(LSE.shape) == (B, H, Nq), "shape mismatch")
-    _need(Q.dtype == K.dtype == V.dtype == O.dtype, "Q, K, V, O must share a dtype")
-    _need(str(LSE.dtype) == "torch.float32", "LSE must be float32")
-    return B, H, Nq, Nk, d
-
-
 def fa_fwd_dropout(Q, K, V, O, LSE, dropout_p, seed, scale=None, causal=False, stream=None) -> None:
-    B, H, Nq, Nk, d = _fwd_check(Q, K, V, O, LSE)
+    B, H, Nq, Nk, d = _check(Q, K, V, O, LSE)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = lib().fa_fwd_dropout(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, H, Nq, Nk, d, float(scale),
@@ -228,13 +232,7 @@ def fa_bwd_workspace_size(B, H, Nq, Nk, d) -> int:
 
 
 def _bwd_args(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal, stream):
-    B, H, Nq, Nk, d = _dims(Q, K)
-    for t in (Q, K, V, O, dO, LSE, dQ, dK, dV, workspace):
-        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
-    _need(K.shape == V.shape == dK.shape == dV.shape and Q.shape == O.shape == dO.shape == dQ.shape,
-          "shape mismatch")
-    _need(len({Q.dtype, K.dtype, V.dtype, O.dtype, dO.dtype, dQ.dtype, dK.dtype, dV.dtype}) == 1,
-          "all tensors except LSE and workspace must share a dtype")
+    B, H, Nq, Nk, d = _check(Q, K, V, O, LSE, dO, dQ, dK, dV, extra=(workspace,))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     nbytes = workspace.numel() * workspace.element_size()

@@ -9,9 +9,11 @@
 
 #include "fa_kernels.hpp"
 
+
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;
+constexpr int kDescribeBytes = 2048;  // fa_describe's buffer (the longest description is well below it)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -120,7 +122,9 @@ fa_status fa_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, f
     float *U = reinterpret_cast<float *>(ws);
     float *M = reinterpret_cast<float *>(ws + pad256(rows * (size_t)d * sizeof(float)));
     float *L = reinterpret_cast<float *>(ws + pad256(rows * (size_t)d * sizeof(float)) + pad256(rows * sizeof(float)));
-    const int n_kt = (Nk + BC - 1) / BC;
+    // under the causal mask only keys 0 .. Nq - 1 can be kept: the ranges cover those
+    const int Nk_used = (causal && Nk > Nq) ? Nq : Nk;
+    const int n_kt = (Nk_used + BC - 1) / BC;
     const int tiles_per_split = (n_kt + num_splits - 1) / num_splits;
     fa::FwdArgs a{Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, causal ? 1 : 0, dtype, stream};
     a.num_splits = num_splits;
@@ -133,7 +137,9 @@ fa_status fa_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, f
 
 int fa_fwd_num_splits(int B, int H, int Nq, int Nk, int d, int causal) {
     if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return 0;
-    (void)causal;
+    // Under the causal mask no query row sees a key past Nq - 1 (key j is kept for
+    // query i only when j <= i), so ranges beyond that would only be empty.
+    if (causal && Nk > Nq) Nk = Nq;
     // Measured on MI355X (one head of 4096 x 4096, d64; 8 heads of one query
     // against 8192 keys; 32 heads of 128 queries against 32768 keys): the
     // best count gives about one workgroup per CU and keeps 8 or more key
@@ -223,10 +229,11 @@ const char *fa_status_string(int status) {
 const char *fa_describe(int d, int dtype, int causal) {
     if ((d != 64 && d != 128) || dtype < FA_BF16 || dtype > FA_F32) return "unsupported";
     static const char *names[] = {"bf16", "f16", "f32"};
-    thread_local char buf[512];
-    snprintf(buf, sizeof buf, "d=%d dtype=%s causal=%d | fwd: %s | bwd: %s", d, names[dtype], causal ? 1 : 0,
-             fa::describe_fwd(), fa::describe_bwd());
-    return buf;
+    thread_local char buf[kDescribeBytes];
+    const int n = snprintf(buf, sizeof buf, "d=%d dtype=%s causal=%d | fwd: %s | bwd: %s", d, names[dtype],
+                           causal ? 1 : 0, fa::describe_fwd(), fa::describe_bwd());
+    // the kernel descriptions are fixed strings: one that did not fit is a bug of this file
+    return (n < 0 || n >= (int)sizeof buf) ? "fa_describe: description longer than its buffer" : buf;
 }
 
 }  // extern "C"
