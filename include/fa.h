@@ -33,8 +33,9 @@
  *  - d must be 64 or 128.  B, H, Nq, Nk >= 1 need not be multiples of any
  *    tile size.  B*H*max(Nq,Nk)*d must stay below 2^31 elements.
  *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls only
- *    enqueue work on it: they do not synchronise, allocate or keep state, and
- *    may be called from several host threads.  fa_bwd must be ordered after
+ *    enqueue work on it: they do not synchronise, allocate or keep state
+ *    (fa_bwd_noalloc's fixed device array aside), and may be called from
+ *    several host threads.  fa_bwd must be ordered after
  *    the fa_fwd that produced O and LSE (same stream, or an event).
  *  - Errors: argument problems are detected on the host before anything is
  *    enqueued and returned as FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED;
@@ -196,6 +197,30 @@ fa_status fa_bwd_stage(int stage, const void *Q, const void *K, const void *V, c
                        const float *LSE, void *dQ, void *dK, void *dV,
                        int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The same kernels and results as
+ * fa_bwd, bit for bit; the D = rowsum(dO * O) rows that fa_bwd keeps in the
+ * caller's workspace live in a fixed device array of the library instead:
+ * FA_NOALLOC_MAX_ROWS floats (16 MiB), one copy per GPU, held until the
+ * process ends.
+ *  - B*H*Nq must not exceed FA_NOALLOC_MAX_ROWS: larger calls return
+ *    FA_ERR_UNSUPPORTED without launching anything.
+ *  - Every call on one GPU uses that GPU's one array, which keeps the last
+ *    call's contents: calls that overlap on one GPU (concurrent streams,
+ *    several host threads without ordering) race and may return wrong
+ *    gradients.  Calls ordered on one stream are safe.
+ *  - The first call on a device (with that device current, hipSetDevice)
+ *    looks the array's device address up once; FA_ERR_HIP if that fails.
+ *  - Everything else (arguments, checks, errors) as fa_bwd.
+ */
+#define FA_NOALLOC_MAX_ROWS (4 * 1024 * 1024)
+fa_status fa_bwd_noalloc(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                         const float *LSE, void *dQ, void *dK, void *dV,
+                         int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                         void *stream);
 
 /* Static string naming the HIP and compiler versions the library was built
  * with and its target, for measurement records. */

@@ -25,7 +25,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert names == ["fa_build_info", "fa_bwd", "fa_bwd_dropout", "fa_bwd_num_stages", "fa_bwd_stage", "fa_bwd_workspace_size",
+    assert names == ["fa_build_info", "fa_bwd", "fa_bwd_dropout", "fa_bwd_noalloc", "fa_bwd_num_stages", "fa_bwd_stage",
+                     "fa_bwd_workspace_size",
                      "fa_describe", "fa_dropout_threshold", "fa_fwd", "fa_fwd_dropout", "fa_fwd_num_splits",
                      "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_workspace_size", "fa_fwd_ws",
                      "fa_status_string"]
@@ -286,3 +287,16 @@ def test_dropout_rejects(lib):
                                              1 << 40, NULL)
     assert bwd(1.2) == fa.FA_ERR_INVALID_ARG
     assert bwd(0.1, ws=NULL) == fa.FA_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects(lib):
+    # argument problems come back before the library looks up its device array
+    # (nothing here initialises the GPU)
+    ok = (P, P, P, P, P, P, P, P, P, 1, 1, 8, 8, 64, 0.125, 0, 0, NULL)
+    bad = lambda i, v: tuple(v if k == i else a for k, a in enumerate(ok))
+    assert lib.fa_bwd_noalloc(*bad(6, NULL)) == fa.FA_ERR_INVALID_ARG     # dQ null
+    assert lib.fa_bwd_noalloc(*bad(0, MIS)) == fa.FA_ERR_INVALID_ARG      # Q misaligned
+    assert lib.fa_bwd_noalloc(*bad(9, 0)) == fa.FA_ERR_INVALID_ARG        # B = 0
+    assert lib.fa_bwd_noalloc(*bad(14, float("inf"))) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_bwd_noalloc(*bad(13, 80)) == fa.FA_ERR_UNSUPPORTED      # d
+    assert lib.fa_bwd_noalloc(*bad(11, fa.FA_NOALLOC_MAX_ROWS + 1)) == fa.FA_ERR_UNSUPPORTED  # rows past the array

@@ -18,6 +18,7 @@ Entry points keep the C names:
     fa_bwd_dropout(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, dropout_p, seed, scale, causal=False, stream=None)
     fa_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal=False, stream=None)
     fa_bwd_workspace_size(B, H, Nq, Nk, d) -> int
+    fa_bwd_noalloc(Q, K, V, O, dO, LSE, dQ, dK, dV, scale, causal=False, stream=None)
     fa_bwd_num_stages() -> int
     fa_bwd_stage(stage, <fa_bwd arguments>)
     fa_status_string(status) -> str
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd.restype = i
     L.fa_build_info.argtypes = []
     L.fa_build_info.restype = ctypes.c_char_p
+    L.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    L.fa_bwd_noalloc.restype = i
     L.fa_bwd_num_stages.argtypes = []
     L.fa_bwd_num_stages.restype = i
     L.fa_bwd_stage.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
@@ -245,6 +248,22 @@ def fa_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale=None, causal=False,
     st = lib().fa_bwd(*_bwd_args(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal, stream))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+
+
+FA_NOALLOC_MAX_ROWS = 4 * 1024 * 1024  # include/fa.h
+
+
+def fa_bwd_noalloc(Q, K, V, O, dO, LSE, dQ, dK, dV, scale=None, causal=False, stream=None) -> None:
+    """fa_bwd without a workspace: D lives in the library's fixed device array
+    (calls that overlap on one GPU race; B*H*Nq <= FA_NOALLOC_MAX_ROWS)."""
+    B, H, Nq, Nk, d = _check(Q, K, V, O, LSE, dO, dQ, dK, dV)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_bwd_noalloc(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK),
+                              _ptr(dV), B, H, Nq, Nk, d, float(scale), int(bool(causal)), dtype_code(Q.dtype),
+                              _stream_handle(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_noalloc")
 
 
 def fa_bwd_num_stages() -> int:

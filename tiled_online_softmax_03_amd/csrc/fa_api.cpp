@@ -7,8 +7,15 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "fa_kernels.hpp"
 
+// Device scratch of fa_bwd_noalloc: the D = rowsum(dO * O) rows live here
+// instead of in a caller workspace.  Each GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` only names the symbol:
+// its device address comes from hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) float scratch[FA_NOALLOC_MAX_ROWS];
 
 namespace {
 
@@ -164,14 +171,19 @@ size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d) {
     return pad256(rows * sizeof(float));
 }
 
+// Pointer checks of the backward: none null, all 16-byte aligned.
+static bool bwd_ptrs_ok(const void *Q, const void *K, const void *V, const void *O, const void *dO, const float *LSE,
+                        const void *dQ, const void *dK, const void *dV) {
+    if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return false;
+    return aligned16(Q) && aligned16(K) && aligned16(V) && aligned16(O) && aligned16(dO) && aligned16(LSE) &&
+           aligned16(dQ) && aligned16(dK) && aligned16(dV);
+}
+
 static fa_status bwd_impl(int stage, const void *Q, const void *K, const void *V, const void *O, const void *dO,
                           const float *LSE, void *dQ, void *dK, void *dV, int B, int H, int Nq, int Nk, int d,
                           float scale, int causal, int dtype, void *workspace, size_t workspace_bytes,
                           void *stream, fa::Dropout drop = make_dropout(0, 0)) {
-    if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV || !workspace) return FA_ERR_INVALID_ARG;
-    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(LSE) ||
-        !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
-        return FA_ERR_INVALID_ARG;
+    if (!workspace || !bwd_ptrs_ok(Q, K, V, O, dO, LSE, dQ, dK, dV)) return FA_ERR_INVALID_ARG;
     if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_INVALID_ARG;
     const fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
     if (st != FA_OK) return st;
@@ -197,6 +209,49 @@ fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, con
                  int dtype, void *workspace, size_t workspace_bytes, void *stream) {
     return bwd_impl(-1, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal, dtype, workspace,
                     workspace_bytes, stream);
+}
+
+// Device address of this GPU's `scratch`, looked up once per device with that
+// device current (the first fa_bwd_noalloc call on it); nullptr if the lookup
+// fails.
+static void *noalloc_scratch(int *hip_err) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *ptr[kMaxDevices];
+    static bool done[kMaxDevices];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *hip_err = 1;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!done[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            *hip_err = 1;
+            return nullptr;  // not cached: a later call tries again
+        }
+        ptr[dev] = p;
+        done[dev] = true;
+    }
+    return ptr[dev];
+}
+
+fa_status fa_bwd_noalloc(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                         const float *LSE, void *dQ, void *dK, void *dV, int B, int H, int Nq, int Nk, int d,
+                         float scale, int causal, int dtype, void *stream) {
+    // the same argument checks as fa_bwd first, so a bad call never touches the scratch
+    if (!bwd_ptrs_ok(Q, K, V, O, dO, LSE, dQ, dK, dV)) return FA_ERR_INVALID_ARG;
+    const fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if ((int64_t)B * H * Nq > (int64_t)FA_NOALLOC_MAX_ROWS) return FA_ERR_UNSUPPORTED;
+    int hip_err = 0;
+    void *ws = noalloc_scratch(&hip_err);
+    if (!ws) return FA_ERR_HIP;
+    return bwd_impl(-1, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal, dtype, ws,
+                    (size_t)FA_NOALLOC_MAX_ROWS * sizeof(float), stream);
 }
 
 int fa_bwd_num_stages(void) { return fa::kBwdStages; }
