@@ -170,6 +170,14 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
     auto load_tile = [&](int qt, int buf) __attribute__((always_inline)) {
         const int q0 = qt * BQ;
         qt_next_row0 = q0;
+        // Only the waves whose threads store the row statistics load them (one
+        // 64-lane load each instead of one per wave), ahead of the copies so
+        // that the copies share the basic block of the products that follow.
+        if (__builtin_amdgcn_readfirstlane(wave) < BQ / 64) {
+            const int qq = min(q0 + (tid & (BQ - 1)), Nq - 1);
+            lreg = LSE[(int64_t)bh * Nq + qq];
+            dvreg = Dvec[(int64_t)bh * Nq + qq];
+        }
         if constexpr (DMA) {
             dma_tile<D, BQ, NW>(Qh, q0, Nq, Qs[buf], wave, lane);
             dma_tile<D, BQ, NW>(dOh, q0, Nq, dOs[buf], wave, lane);
@@ -187,9 +195,6 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
                 }
             }
         }
-        const int qq = min(q0 + (tid & (BQ - 1)), Nq - 1);
-        lreg = LSE[(int64_t)bh * Nq + qq];
-        dvreg = Dvec[(int64_t)bh * Nq + qq];
     };
     auto store_tile = [&](int buf) __attribute__((always_inline)) {
         if constexpr (!DMA) {
@@ -224,7 +229,9 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
     auto step = [&](int qt, auto buf_c) __attribute__((always_inline)) {
         constexpr int buf = decltype(buf_c)::value;
         const bool more = qt + 1 < n_qt;
-        if (more) load_tile(qt + 1, buf ^ 1);  // in flight during this step's math
+        // The prefetch goes out on every step (the last step copies its own tile
+        // into the idle buffer again): no branch separates it from the products.
+        load_tile(more ? qt + 1 : qt, buf ^ 1);  // in flight during this step's math
         const uint16_t *qs = Qs[buf];
         const uint16_t *ds = dOs[buf];
         // (The d = 128 branch keeps a single block in this exact form: the compiler's
@@ -347,7 +354,7 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
                 }
             }
         }
-        if (more) store_tile(buf ^ 1);
+        store_tile(buf ^ 1);
         wait_vmem();
         __syncthreads();
     };

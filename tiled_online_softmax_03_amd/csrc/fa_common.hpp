@@ -199,7 +199,9 @@ __device__ __forceinline__ void dma_tile(const void *g, int row0, int nrows, uin
     static_assert(R % RPB == 0, "tile rows must fill whole 1 KiB blocks");
     const int r_in = lane / (W / 8), p = lane % (W / 8);
 #pragma unroll
-    for (int b = wave; b < NBLK; b += NWAVES) {
+    for (int j = 0; j < (NBLK + NWAVES - 1) / NWAVES; ++j) {
+        const int b = wave + j * NWAVES;
+        if (NBLK % NWAVES != 0 && b >= NBLK) break;
         const int r = b * RPB + r_in;
         const int c = p ^ swz<W>(r);
         int grow = row0 + r;
