@@ -32,11 +32,12 @@
  * exp/log.  Summation order is the plain ascending order of the index being
  * summed; nothing is blocked, fused or reordered.
  *
- * oracle_online_row / oracle_tiled_fwd follow the running-state recurrence of
- * research-attention section 02 (state m, l, u; merge with alpha = exp(m - m'),
- * p_j = exp(s_j - m'); init (-inf, 0, 0); one division at the end), in the
- * page's notation, for checking the tiled/untiled agreement and the worked
- * row's intermediate state.
+ * oracle_online_row / oracle_tiled_fwd build the result from running states
+ * (research-attention section 02): each tile of keys gets its own state
+ * (m_t, l_t, u_t), the tiles are folded into the row's state one after the
+ * other with that section's rule for combining two states, and o = u / l with
+ * one division at the end.  They serve the tiled/untiled agreement check and
+ * the worked row's intermediate state.
  *
  * All arrays are contiguous row-major: Q [B,H,Nq,d], K/V [B,H,Nk,d],
  * O/dO/dQ [B,H,Nq,d], dK/dV [B,H,Nk,d], LSE [B,H,Nq].  Returns 0 on success,
@@ -242,34 +243,63 @@ int oracle_bwd(const double *Q, const double *K, const double *V, const double *
     return 0;
 }
 
+/* The state of one tile of keys [a, b) on its own (research-attention, section
+ * 02: the three quantities a block contributes): its maximum m_t, its sum
+ * l_t = sum_j exp(s_j - m_t) and its unnormalised output u_t = sum_j
+ * exp(s_j - m_t) v_j. */
+static void tile_state(const double *s, const double *v, int64_t a, int64_t b, int64_t dv, double *m_t,
+                       double *l_t, double *u_t) {
+    double mx = -INFINITY;
+    for (int64_t j = a; j < b; ++j) mx = s[j] > mx ? s[j] : mx;
+    double sum = 0.0;
+    for (int64_t c = 0; c < dv; ++c) u_t[c] = 0.0;
+    for (int64_t j = a; j < b; ++j) {
+        const double w = exp(s[j] - mx);
+        sum += w;
+        for (int64_t c = 0; c < dv; ++c) u_t[c] += w * v[j * dv + c];
+    }
+    *m_t = mx;
+    *l_t = sum;
+}
+
+/* Section 02's rule for combining two states into the first: with
+ * m = max(m1, m2), each side's l and u are weighted by exp(m_k - m) and added.
+ * The empty state (nothing seen yet: l = 0) takes the other state as it is. */
+static void merge_state(double *m1, double *l1, double *u1, double m2, double l2, const double *u2, int64_t dv) {
+    if (*l1 == 0.0) {
+        *m1 = m2;
+        *l1 = l2;
+        for (int64_t c = 0; c < dv; ++c) u1[c] = u2[c];
+        return;
+    }
+    const double m = *m1 > m2 ? *m1 : m2;
+    const double w_old = exp(*m1 - m), w_new = exp(m2 - m);
+    *l1 = w_old * *l1 + w_new * l2;
+    for (int64_t c = 0; c < dv; ++c) u1[c] = w_old * u1[c] + w_new * u2[c];
+    *m1 = m;
+}
+
 /*
- * Running-state recurrence for one row (research-attention, section 02):
- * scores s[0..n), value rows v[n][dv].  Processes the first `ntiles` tiles of
- * `tile` consecutive scores (all of them when ntiles < 0) starting from the
- * state (m, l, u) = (-inf, 0, 0), and returns that state unnormalised.
+ * Running state of one row (research-attention, section 02): scores s[0..n),
+ * value rows v[n][dv].  Folds the states of the first `ntiles` tiles of `tile`
+ * consecutive scores (all of them when ntiles < 0) into the empty state, in
+ * order, and returns the result (m, l, u) unnormalised.
  */
 int oracle_online_row(const double *s, const double *v, int64_t n, int64_t dv, int64_t tile,
                       int64_t ntiles, double *m_out, double *l_out, double *u_out) {
     if (!s || !v || !m_out || !l_out || !u_out || n <= 0 || dv <= 0 || tile <= 0) return -1;
-    double m = -INFINITY, l = 0.0;
+    double *u_t = (double *)malloc(sizeof(double) * (size_t)dv);
+    if (!u_t) return -2;
+    double m = -INFINITY, l = 0.0;  /* the empty state */
     for (int64_t c = 0; c < dv; ++c) u_out[c] = 0.0;
-    int64_t done = 0;
-    for (int64_t start = 0; start < n && (ntiles < 0 || done < ntiles); start += tile, ++done) {
-        const int64_t end = start + tile < n ? start + tile : n;
-        double block_max = -INFINITY;
-        for (int64_t j = start; j < end; ++j)
-            if (s[j] > block_max) block_max = s[j];
-        const double m_new = m > block_max ? m : block_max;
-        const double alpha = exp(m - m_new);
-        l *= alpha;
-        for (int64_t c = 0; c < dv; ++c) u_out[c] *= alpha;
-        for (int64_t j = start; j < end; ++j) {
-            const double p = exp(s[j] - m_new);
-            l += p;
-            for (int64_t c = 0; c < dv; ++c) u_out[c] += p * v[j * dv + c];
-        }
-        m = m_new;
+    const int64_t tiles = (n + tile - 1) / tile;
+    for (int64_t t = 0; t < tiles && (ntiles < 0 || t < ntiles); ++t) {
+        const int64_t a = t * tile, b = a + tile < n ? a + tile : n;
+        double m_t, l_t;
+        tile_state(s, v, a, b, dv, &m_t, &l_t, u_t);
+        merge_state(&m, &l, u_out, m_t, l_t, u_t, dv);
     }
+    free(u_t);
     *m_out = m;
     *l_out = l;
     return 0;

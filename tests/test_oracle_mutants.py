@@ -27,10 +27,12 @@ MUTANTS = [
     ("no_scale_in_S", "row[j] = scale * dot(Q + i * d, K + j * d, d);", "row[j] = dot(Q + i * d, K + j * d, d);"),
     ("sum_without_shift", "if (allowed(i, j, causal)) l += exp(row[j] - m);", "if (allowed(i, j, causal)) l += exp(row[j]);"),
     ("lse_sign", "LSE[i] = m + log(l);", "LSE[i] = m - log(l);"),
-    ("online_l_not_rescaled", "    l *= alpha;\n", "    l *= 1.0;\n"),
-    ("online_u_not_rescaled", "u_out[c] *= alpha;", "u_out[c] *= 1.0;"),
-    ("online_alpha_sign", "const double alpha = exp(m - m_new);", "const double alpha = exp(m_new - m);"),
-    ("online_p_old_max", "const double p = exp(s[j] - m_new);", "const double p = exp(s[j] - m);"),
+    ("online_l_old_unweighted", "*l1 = w_old * *l1 + w_new * l2;", "*l1 = *l1 + w_new * l2;"),
+    ("online_u_old_unweighted", "u1[c] = w_old * u1[c] + w_new * u2[c];", "u1[c] = u1[c] + w_new * u2[c];"),
+    ("online_weight_sign", "const double w_old = exp(*m1 - m), w_new = exp(m2 - m);",
+     "const double w_old = exp(m - *m1), w_new = exp(m - m2);"),
+    ("online_tile_unshifted", "const double w = exp(s[j] - mx);", "const double w = exp(s[j]);"),
+    ("online_max_not_kept", "    *m1 = m;\n}", "    *m1 = m2;\n}"),
     ("rows_no_mask", "if (!allowed(i, j, causal)) continue;\n                const double p", "const double p"),
     ("philox_key_not_bumped", "            k1 += kPhiloxWeyl1;\n", "            k1 += 0u;\n"),
     ("philox_hi_for_lo", "        c1 = lo1;", "        c1 = hi1;"),
