@@ -13,7 +13,7 @@ oracle timed on a bounded sample of the same workload on this host).
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload NAME]
                     [--no-cpu-baseline] [--cpu-heads 48] [--copy-probe-mib 0]
                     [--no-sclk]
-    python bench.py --memory-sweep     (forward peak memory against N, one JSON line)
+    python bench.py --memory-sweep     (peak memory of a whole step against N, one JSON line)
 """
 from __future__ import annotations
 
@@ -56,8 +56,8 @@ def parse():
                     help="forward through fa_fwd_splitkv with this many key ranges ('auto' = "
                          "fa_fwd_num_splits); implies --fwd-only")
     ap.add_argument("--memory-sweep", action="store_true",
-                    help="instead of the step benchmark: forward peak memory and time at B1 H32 d128 for "
-                         "N = 4096 .. 65536")
+                    help="instead of the step benchmark: peak memory and time of a whole step at B1 H32 "
+                         "d128 for N = 4096 .. 65536")
     return ap.parse_args()
 
 
@@ -95,6 +95,12 @@ def main():
     LSE = torch.empty((w.B, w.H, w.Nq), device=dev, dtype=torch.float32)
     stream = torch.cuda.current_stream()
     splits = None
+    if args.splits is None and fwd_only and not args.fwd_plain and args.dropout <= 0:
+        # forward-only shapes with too few query tiles for 256 CUs (one head of 4096 rows)
+        # take the split-KV forward, the library's path for them
+        auto = fa.fa_fwd_num_splits(w.B, w.H, w.Nq, w.Nk, w.d, w.causal)
+        if auto > 1:
+            args.splits = "auto"
     if args.splits is not None:
         splits = (fa.fa_fwd_num_splits(w.B, w.H, w.Nq, w.Nk, w.d, w.causal) if args.splits == "auto"
                   else int(args.splits))
@@ -328,9 +334,11 @@ def cpu_model():
 
 
 def memory_sweep():
-    """Forward-only peak device memory and time at B1 H32 d128, bf16,
-    non-causal, for N = 4096 .. 65536, against the size one materialised
-    bf16 score matrix would take."""
+    """Peak device memory and time of one whole step (fa_fwd_ws + fa_bwd, every
+    buffer caller-owned: inputs, outputs, both workspaces) at B1 H32 d128, bf16,
+    non-causal, for N = 4096 .. 65536, against the size one materialised bf16
+    score matrix would take.  The library allocates nothing itself, so torch's
+    peak-allocated counter sees every byte."""
     import torch
 
     import synth
@@ -339,34 +347,44 @@ def memory_sweep():
     fa.lib()
     dev = torch.device("cuda:0")
     rows = []
+    B, H, d = 1, 32, 128
     for n in (4096, 8192, 16384, 32768, 65536):
         torch.cuda.empty_cache()
         torch.cuda.synchronize()
         base = torch.cuda.memory_allocated()
-        inp = synth.make_inputs(1, 32, n, n, 128, "bf16", seed=7000 + n, device=dev, with_dO=False)
-        Q, K, V = inp["Q"], inp["K"], inp["V"]
+        torch.cuda.reset_peak_memory_stats()
+        inp = synth.make_inputs(B, H, n, n, d, "bf16", seed=7000 + n, device=dev)
+        Q, K, V, dO = inp["Q"], inp["K"], inp["V"], inp["dO"]
         O = torch.empty_like(Q)
-        LSE = torch.empty((1, 32, n), device=dev, dtype=torch.float32)
-        scale = 128 ** -0.5
+        LSE = torch.empty((B, H, n), device=dev, dtype=torch.float32)
+        dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+        ws_f = torch.empty(fa.fa_fwd_workspace_size(B, H, n, n, d), device=dev, dtype=torch.uint8)
+        ws_b = fa.alloc_workspace(Q, K)
+        scale = d ** -0.5
         stream = torch.cuda.current_stream()
-        torch.cuda.synchronize()
-        torch.cuda.reset_peak_memory_stats()  # from here on: what the forward itself needs
-        fa.fa_fwd(Q, K, V, O, LSE, scale, False, stream)
+
+        def step():
+            fa.fa_fwd_ws(Q, K, V, O, LSE, ws_f, scale, False, stream)
+            fa.fa_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, ws_b, scale, False, stream)
+
+        step()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        reps = 3
+        reps = 2
         for _ in range(reps):
-            fa.fa_fwd(Q, K, V, O, LSE, scale, False, stream)
+            step()
         e1.record(stream)
         torch.cuda.synchronize()
         peak = torch.cuda.max_memory_allocated() - base
         ms = e0.elapsed_time(e1) / reps
-        flops = 4.0 * 32 * n * n * 128
-        rows.append({"N": n, "peak_bytes": peak, "inputs_outputs_bytes": 4 * 32 * n * 128 * 2 + 32 * n * 4,
-                     "materialised_S_bf16_bytes": 32 * n * n * 2, "fwd_ms": ms, "fwd_tflops": flops / ms / 1e9})
-        del inp, Q, K, V, O, LSE
-    print(json.dumps({"memory_sweep": "fa_fwd, B1 H32 d128 bf16, non-causal", "rows": rows,
+        flops = 3.5 * 4.0 * B * H * n * n * d
+        rows.append({"N": n, "peak_bytes": peak,
+                     "workspace_bytes": ws_f.numel() + ws_b.numel(),
+                     "materialised_S_bf16_bytes": B * H * n * n * 2, "step_ms": ms, "step_tflops": flops / ms / 1e9})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        del inp, Q, K, V, dO, O, LSE, dQ, dK, dV, ws_f, ws_b
+    print(json.dumps({"memory_sweep": "fa_fwd_ws + fa_bwd, B1 H32 d128 bf16, non-causal", "rows": rows,
                       "device": torch.cuda.get_device_properties(0).gcnArchName}), flush=True)
 
 

@@ -28,6 +28,15 @@
  *    FA_F32 reads and writes float32 but rounds the matrix-core operands
  *    (Q, K, V, dO, and the probabilities) to 16-bit first, so it is not a
  *    true-fp32 attention.  Accumulation is float32 in every mode.
+ *  - The forward multiplies the probabilities with V on the fp16 matrix core,
+ *    converting bf16 (and bf16-rounded fp32) V to fp16: V must satisfy
+ *    |V| <= 65504, the fp16 range (for bf16 data: |V| <= 65280, the largest
+ *    bf16 number in it).  Inside that range the conversion is exact down to
+ *    2^-14, and below that it keeps fp16's subnormal precision (absolute
+ *    error <= 2^-25).  A larger value becomes infinity there, and every
+ *    output row that gives its key weight comes out non-finite; no error is
+ *    returned (the library does not read V on the host).  The backward is
+ *    not limited by this.
  *  - causal != 0 keeps key j for query i exactly when j <= i (top-left
  *    alignment, for any Nq and Nk).  Key 0 is always kept, so no row is empty.
  *  - d must be 64 or 128.  B, H, Nq, Nk >= 1 need not be multiples of any

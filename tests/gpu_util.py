@@ -138,3 +138,30 @@ def zero_grad_bound(O, dO, K, Q, scale, dtype):
 
 def scale_of(d):
     return 1.0 / math.sqrt(d)
+
+
+ROW_REL = 1.5e-2  # per-row relative L2 error of a gradient row (global bar 5e-3)
+
+
+def check_rows(got, ref, label="", bar=ROW_REL):
+    """Per-row relative error of each gradient (rows of dQ, dK, dV: the last
+    axis is the head dim).  Every row must satisfy
+        ||got_row - ref_row|| <= bar * max(||ref_row||, median row norm / 4)
+    so a single wrong row fails even where the global rel-L2 (dominated by
+    millions of correct elements) would not; the floor keeps rows whose exact
+    gradient is nearly zero from failing on rounding alone.  Returns the worst
+    ratio per tensor."""
+    worst = {}
+    for k in ("dQ", "dK", "dV"):
+        g = got[k].reshape(-1, got[k].shape[-1])
+        r = ref[k].reshape(-1, ref[k].shape[-1])
+        err = np.linalg.norm(g - r, axis=1)
+        nrm = np.linalg.norm(r, axis=1)
+        floor = max(float(np.median(nrm)) / 4.0, 1e-30)
+        ratio = err / np.maximum(nrm, floor)
+        worst[k] = float(np.max(ratio))
+        worst[k + "_row"] = int(np.argmax(ratio))
+    say("    per-row", label, " ".join("%s=%.3g" % (k, v) for k, v in worst.items() if not k.endswith("_row")))
+    for k in ("dQ", "dK", "dV"):
+        assert worst[k] <= bar, (label, k, worst)
+    return worst
