@@ -209,7 +209,7 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
         if (tid < BQ) {
             const bool real = qt_next_row0 + tid < Nq;
             lse2[buf][tid] = real ? lreg * kLog2e : INFINITY;  // P = 0 on padding rows
-            dvec[buf][tid] = real ? dvreg : 0.f;
+            dvec[buf][tid] = real ? (DROP ? dvreg : -dvreg) : 0.f;  // -D: the dP chains start from it
         }
     };
 
@@ -243,6 +243,14 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
             if (!CAUSAL || q0 + 31 >= kw0) {  // else every row of the block precedes this wave's keys
                 // S = Q K^T and dP = dO V^T: lane = key, register r -> query q0 + 8*(r/4) + 4*g + r%4
                 f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+                if constexpr (!DROP) {
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const f32x4_t D4 = *reinterpret_cast<const f32x4_t *>(&dvec[buf][qh * 32 + 8 * rq + 4 * g]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dp[4 * rq + i] = D4[i];  // -D of the block's rows
+                    }
+                }
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
                     const int qoff = tile_off<D>(qh * 32 + l32, 16 * ks + 8 * g);
@@ -273,7 +281,7 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
                             t[i] = pv * ((kept ? dp[r] * dr.keep_scale : 0.f) - D4[i]);
                         } else {
                             p[i] = pv;
-                            t[i] = pv * (dp[r] - D4[i]);
+                            t[i] = pv * dp[r];  // dp holds dP - D
                         }
                     }
                     pp[2 * rq] = pack_in<E>(p[0], p[1]);
@@ -302,6 +310,14 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
                 if (!CAUSAL || q0 + 31 >= kw0) {  // else every row of the block precedes this wave's keys
                     // S = Q K^T and dP = dO V^T: lane = key, register r -> query q0 + 8*(r/4) + 4*g + r%4
                     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+                    if constexpr (!DROP) {
+#pragma unroll
+                        for (int rq = 0; rq < 4; ++rq) {
+                            const f32x4_t D4 = *reinterpret_cast<const f32x4_t *>(&dvec[buf][r0 + 8 * rq + 4 * g]);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) dp[4 * rq + i] = D4[i];  // -D of the block's rows
+                        }
+                    }
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) {
                         const int qoff = tile_off<D>(r0 + l32, 16 * ks + 8 * g);
@@ -332,7 +348,7 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
                                 t[i] = pv * ((kept ? dp[r] * dr.keep_scale : 0.f) - D4[i]);
                             } else {
                                 p[i] = pv;
-                                t[i] = pv * (dp[r] - D4[i]);
+                                t[i] = pv * dp[r];  // dp holds dP - D
                             }
                         }
                         pp[2 * rq] = pack_in<E>(p[0], p[1]);
