@@ -18,8 +18,16 @@ LIB = os.path.join(HERE, "libfa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
-# Per-source extra flags (none needed by default; variants for measurements set them).
-EXTRA = {}
+# Per-source extra flags.  fa_bwd.hip: matrix products write VGPRs unless a
+# kernel pins an accumulator to AGPRs itself (bwd_dkdv_kv_kernel keeps dV/dK in
+# AGPRs and needs S/dP in VGPRs, where its softmax reads them; the other
+# kernels of the file use no AGPRs and compile to the same code either way).
+EXTRA = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
+def device_flags(src: str) -> list:
+    """The flags every device compile of `src` uses (the build and the resource check)."""
+    return [*DEVICE, *EXTRA.get(src, [])]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -31,7 +39,7 @@ DEVICE = ["-x", "hip", "--offload-arch=" + ARCH, "-munsafe-fp-atomics",
 def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD_DIR, src + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE, *EXTRA.get(src, []), "-c", path, "-o", obj]
+    cmd = [HIPCC, *COMMON, *device_flags(src), "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -19,7 +19,10 @@
 //                       accumulating dV^T += dO^T P and dK^T += Q^T dS in
 //                       registers.  Q and dO are staged row-major through LDS
 //                       (double-buffered); their transposes are read with
-//                       ds_read_b64_tr_b16.
+//                       ds_read_b64_tr_b16.  For d = 128 16-bit data without
+//                       dropout, bwd_dkdv_kv_kernel does the same with four
+//                       waves, one per SIMD, whose K and V fragments stay in
+//                       registers for the whole pass.
 //   2. bwd_dq_kernel    Q-stationary: a workgroup owns 256 query rows (32 per
 //                       wave, Q and dO rows held in VGPRs) and streams K/V
 //                       tiles like the forward: S^T = K Q^T, dP^T = V dO^T,
@@ -40,6 +43,11 @@
 // Query rows per step of the dK/dV pass at d = 64 (64 at d = 128).
 #ifndef FA_DKDV_ROWS_D64
 #define FA_DKDV_ROWS_D64 128
+#endif
+// The d = 128 16-bit dK/dV pass without dropout keeps K and V in registers
+// (bwd_dkdv_kv_kernel); 0 selects the two-waves-per-SIMD pass for it too.
+#ifndef FA_DKDV_KV
+#define FA_DKDV_KV 1
 #endif
 
 namespace fa {
@@ -413,6 +421,320 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
     }
 }
 
+// ---------------------------------------------------------------- 1'. dK, dV with K and V in registers
+// The d = 128 16-bit pass without dropout.  Four waves, one per SIMD, each
+// owning 32 keys for the whole pass, so its K and V fragments (the B operands
+// of S = Q K^T and dP = dO V^T) stay in registers and the only LDS operands
+// are the streamed Q and dO rows: a third less LDS traffic per product than
+// the two-waves-per-SIMD pass above, which reads K and V from LDS.  With one
+// wave per SIMD nothing hides a stall but the wave's own instruction stream,
+// so the step is written as a fixed program:
+//  * V is held negated: the dP accumulator starts from D and ends as D - dP,
+//    so dS = P (dP - D) = -(P * acc) is one multiply per element; dK is
+//    accumulated with that sign and flipped together with the final scale.
+//  * dV^T and dK^T accumulate in AGPRs (mfma_acc), the S and dP products in
+//    VGPRs where the softmax gradient reads them.
+//  * Q and dO tiles of BQ rows are double-buffered in LDS.  The copies
+//    global -> LDS are issued as inline assembly, invisible to the compiler,
+//    which would otherwise wait for them before the first transposed LDS read
+//    of the step (it cannot tell that read from the copy's target); the step
+//    waits for them once, at its end, before the barrier.  (The compiler uses
+//    no M0 of its own in this kernel, so the copies may set it.)
+//  * A step is BQ / 32 row blocks; each block is 16 S/dP products (A) and 16
+//    dV/dK products (B), ordered A0 A1 B0 A2 B1 ... so that every block's
+//    softmax gradient runs beside the products of the next group, one pair
+//    of elements per two products; the LDS operand of each product is read
+//    LEAD products ahead.  A scheduling barrier after every product keeps
+//    this order.
+//  * LDS addresses are one per-lane offset per operand shape plus an
+//    immediate (tensor and row block); the stage is added once per step.
+#ifndef FA_KV_ROWS
+#define FA_KV_ROWS 64  // query rows per step (128 measured 2 % slower)
+#endif
+#ifndef FA_KV_LEAD
+#define FA_KV_LEAD 3
+#endif
+template <int E, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, const void *__restrict__ V,
+                        const void *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Dvec,
+                        void *__restrict__ dK, void *__restrict__ dV, int BH, int Nq, int Nk, float scale,
+                        float scale_log2, int n_kt) {
+    constexpr int D = 128, NW = 4, BQ = FA_KV_ROWS, BKC = 32 * NW;
+    constexpr int NB = BQ / 32;       // 32-row blocks per step
+    constexpr int NP = 32 * NB;       // matrix products per step
+    constexpr int NKS = D / 16;       // k-steps over the head dim
+    constexpr int NDB = D / 32;       // 32-row blocks of dK^T / dV^T
+    constexpr int TILE = BQ * D * 2;  // bytes of one tile of BQ rows
+    constexpr int NCP = BQ / 16;      // 1 KiB copies per wave per tensor per tile
+    constexpr int ST = 4 * TILE;      // row statistics: stage s at ST + s * 8 BQ (LSE * log2 e, then D)
+    constexpr int LEAD = FA_KV_LEAD, NSLOT = LEAD + 1;
+    static_assert(E != ELT_F32, "16-bit operands are copied global -> LDS as they are");
+    static_assert(BQ == 64 || BQ == 128, "two or four row blocks per step");
+    static_assert(BQ * 2 == 64 * NW || BQ == 64 * NW / 4, "one statistics row of 64 per wave or half the waves");
+    // stage s: Q at 2 s TILE, dO at (2 s + 1) TILE
+    __shared__ __attribute__((aligned(16))) unsigned char lds[ST + 2 * 8 * BQ + 512];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, g = lane >> 5;
+
+    int bh, kt;
+    if constexpr (CAUSAL) {
+        const int L = blockIdx.x;  // low key tiles meet the most query rows: first
+        kt = L / BH;
+        bh = L % BH;
+    } else {
+        const int L = xcd_remap(blockIdx.x, gridDim.x);
+        bh = L / n_kt;
+        kt = L % n_kt;
+    }
+    const int64_t q_head = (int64_t)bh * Nq * D;
+    const int64_t k_head = (int64_t)bh * Nk * D;
+    const int k0 = kt * BKC;
+    const int kw0 = k0 + wave * 32;  // first key of this wave
+    const int kw = kw0 + l32;        // this lane's key
+    const int kw_ld = kw < Nk ? kw : Nk - 1;  // keys past Nk compute on a real row and are never stored
+
+    const int n_qt = (Nq + BQ - 1) / BQ;
+    const int qt_begin = CAUSAL ? min(k0 / BQ, n_qt) : 0;  // earlier rows see none of these keys
+
+    // K and -V fragments: lane = key, k = head-dim index 16*ks + 8*g + v.
+    u32x4_t kf[NKS], vn[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        kf[ks] = load8_operand<E>(K, k_head + (int64_t)kw_ld * D + 16 * ks + 8 * g);
+        const u32x4_t v = load8_operand<E>(V, k_head + (int64_t)kw_ld * D + 16 * ks + 8 * g);
+        vn[ks] = v ^ 0x80008000u;  // sign of both 16-bit halves
+    }
+
+    // Per-lane LDS byte offsets in a tile (tile_off<128> layout):
+    //  a_off[ks]: the A operand (row l32, head dims 16ks + 8g .. +7);
+    //  t_off[db][hf]: the transposed read of rows 4g + j/4 + 8 hf, columns
+    //  32 db + 16 ((lane / 16) % 2) + 4 (j % 4), j = lane % 16.
+    uint32_t a_off[NKS], t_off[NDB][2];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) a_off[ks] = 2u * (uint32_t)tile_off<D>(l32, 16 * ks + 8 * g);
+    {
+        const int j = lane & 15;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                t_off[db][hf] = 2u * (uint32_t)tile_off<D>(4 * g + (j >> 2) + 8 * hf, 32 * db + 16 * ((lane >> 4) & 1) + 4 * (j & 3));
+    }
+    const uint32_t st_off = (uint32_t)ST + 16u * (uint32_t)g;  // statistics of rows 4g + 8 rq + i
+
+    // Copies of a tile: blocks of 4 rows (1 KiB), NCP per wave per tensor;
+    // lane l fetches row 4b + l/16, 16-byte chunk (l % 16) ^ swz(row), which the
+    // swizzle places at byte 16 l of the block.  Block b = wave + 4 jb, so the
+    // swizzle of a lane's row is the same for every jb.
+    const uint16_t *Qh = static_cast<const uint16_t *>(Q) + q_head;
+    const uint16_t *dOh = static_cast<const uint16_t *>(dO) + q_head;
+    const int cp_row = wave * 4 + lane / 16;  // + 16 jb
+    const uint32_t cp_col = (uint32_t)((lane & 15) ^ swz<D>(cp_row)) * 16u;  // byte offset of the chunk in its row
+    // Row statistics of a tile: wave w loads 64 rows of one of them (LSE for
+    // w < NW / 2, D for the rest; at BQ = 64 waves 1 and 3 load rows nobody
+    // uses), one value per lane.
+    const int st_kind = wave / (NW / 2), st_part = wave % (NW / 2);
+    const float *st_src = (st_kind == 0 ? LSE : Dvec) + (int64_t)bh * Nq;
+    float sreg = 0.f;
+    int st_row0 = 0;
+    auto fetch_stats = [&](int qt) __attribute__((always_inline)) {
+        st_row0 = qt * BQ + 64 * st_part;
+        sreg = st_src[min(st_row0 + lane, Nq - 1)];
+    };
+    // copy jb of this wave's share of the Q and dO rows of tile qt, into stage s
+    auto fetch_copy = [&](int qt, int s, int jb) __attribute__((always_inline)) {
+        const int grow = min(qt * BQ + cp_row + 16 * jb, Nq - 1);  // rows past Nq re-read row Nq - 1 (zero weight)
+        const uint32_t off = (uint32_t)grow * (uint32_t)(D * 2) + cp_col;  // bytes from the head's first row
+        const uint32_t dq = (uint32_t)(2 * s * TILE + (wave + NW * jb) * 1024);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 in the clobber list: see the kernel's notes
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(Qh), "s"(dq)
+                     : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(dOh),
+                     "s"(dq + (uint32_t)TILE)
+                     : "memory", "m0");
+#pragma clang diagnostic pop
+    };
+    // The statistics of the last fetch into stage s, once their loads landed
+    // (a store in every wave: no branch sinks the loads to the end of the
+    // step).  Rows past Nq get LSE = inf (P = 0) and D = 0.
+    auto put_stats = [&](int s) __attribute__((always_inline)) {
+        const bool real = st_row0 + lane < Nq;
+        const float v = st_kind == 0 ? (real ? sreg * kLog2e : INFINITY) : (real ? sreg : 0.f);
+        uint32_t at = (uint32_t)(ST + s * 8 * BQ + st_kind * 4 * BQ + 256 * st_part);
+        if (256 * st_part >= 4 * BQ) at = (uint32_t)(ST + 2 * 8 * BQ + 256 * st_kind);  // unused rows (BQ = 64)
+        *reinterpret_cast<float *>(lds + at + 4 * lane) = v;
+    };
+
+    f32x16_t dvT[NDB], dkT[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) { dvT[db] = f32x16_t{}; dkT[db] = f32x16_t{}; }
+
+    if (qt_begin < n_qt) {
+        fetch_stats(qt_begin);
+#pragma unroll
+        for (int jb = 0; jb < NCP; ++jb) fetch_copy(qt_begin, 0, jb);
+        wait_vmem();
+        put_stats(0);
+    }
+    wait_vmem();
+    __syncthreads();
+    asm volatile("s_nop 3" ::: "memory");  // the zeroed accumulators, before mfma_acc reads them
+
+    // Position of group G (16 products) in the step's order A0 A1 B0 A2 B1 ... B(NB-1):
+    // is it an A group, and of which block.
+    auto grp_is_a = [](int G) constexpr { return G == 0 || (G != 2 * NB - 1 && G % 2 == 1); };
+    auto grp_block = [](int G) constexpr { return G == 0 ? 0 : G == 2 * NB - 1 ? NB - 1 : G % 2 == 1 ? (G + 1) / 2 : (G - 2) / 2; };
+    // first product of A(b); the softmax gradient of block b starts one product
+    // into the group after A(b)
+    auto a_start = [](int b) constexpr { return b == 0 ? 0 : 16 * (2 * b - 1); };
+    auto v_start = [](int b) constexpr { return b == 0 ? 17 : 16 * 2 * b + 1; };
+
+    // One query tile in stage s (its statistics at offset 8 BQ s); the next
+    // tile's copies go into the other stage, which every wave finished reading
+    // before this step's barrier.  MASK: apply the causal mask (the tile
+    // reaches this workgroup's keys).
+    auto step_pipe = [&](int qt, int s, int qn, auto mask_c) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_c)::value;
+        const uint32_t sb = (uint32_t)(2 * s * TILE), stb = (uint32_t)(s * 8 * BQ);
+        uint32_t ao[NKS], to[NDB][2];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) ao[ks] = a_off[ks] + sb;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) { to[db][0] = t_off[db][0] + sb; to[db][1] = t_off[db][1] + sb; }
+        const uint32_t so = st_off + stb;
+        const int q0 = qt * BQ;
+        u32x4_t opr[NSLOT];
+        f32x16_t sc[NB], dp[NB];
+        f32x4_t L4[NB][4];
+        float pv[NB][16], tv[NB][16];
+        uint32_t pp[NB][8], dd[NB][8];
+        // operand of product i into its slot
+        auto rd = [&](int i) __attribute__((always_inline)) {
+            const int G = i / 16, j = i % 16, b = grp_block(G);
+            if (grp_is_a(G)) {  // S / dP of block b: one 16-byte read
+                const int ks = j / 2, w = j % 2;
+                opr[i % NSLOT] = *reinterpret_cast<const u32x4_t *>(lds + ao[ks] + w * TILE + b * 32 * 256);
+            } else {  // dV / dK of block b: two transposed reads
+                const int h = j / 8, db = (j % 8) / 2, w = j % 2;
+                const unsigned off = (w == 0 ? TILE : 0) + (b * 32 + 16 * h) * 256;
+                const u32x2_t x0 = ds_read_tr16(reinterpret_cast<const uint16_t *>(lds + to[db][0] + off));
+                const u32x2_t x1 = ds_read_tr16(reinterpret_cast<const uint16_t *>(lds + to[db][1] + off));
+                opr[i % NSLOT] = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
+            }
+        };
+        auto mm = [&](int i) __attribute__((always_inline)) {
+            const int G = i / 16, j = i % 16, b = grp_block(G);
+            const u32x4_t a = opr[i % NSLOT];
+            if (grp_is_a(G)) {
+                const int ks = j / 2, w = j % 2;
+                if (w == 0) sc[b] = mfma_in<E>(a, kf[ks], ks == 0 ? f32x16_t{} : sc[b]);
+                else dp[b] = mfma_in<E>(a, vn[ks], dp[b]);
+            } else {
+                const int h = j / 8, db = (j % 8) / 2, w = j % 2;
+                if (w == 0) mfma_acc<E>(dvT[db], a, u32x4_t{pp[b][4 * h], pp[b][4 * h + 1], pp[b][4 * h + 2], pp[b][4 * h + 3]});
+                else mfma_acc<E>(dkT[db], a, u32x4_t{dd[b][4 * h], dd[b][4 * h + 1], dd[b][4 * h + 2], dd[b][4 * h + 3]});
+            }
+        };
+        // D of block b's rows into its dP accumulator; LSE * log2 e of its rows
+        auto rd_dinit = [&](int b, int rq) __attribute__((always_inline)) {
+            const f32x4_t D4 = *reinterpret_cast<const f32x4_t *>(lds + so + 4 * BQ + 4 * (32 * b + 8 * rq));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dp[b][4 * rq + k] = D4[k];
+        };
+        auto rd_lse = [&](int b, int rq) __attribute__((always_inline)) {
+            L4[b][rq] = *reinterpret_cast<const f32x4_t *>(lds + so + 4 * (32 * b + 8 * rq));
+        };
+        // elements e, e + 1 of block b's softmax gradient in two halves, each
+        // pair of instructions independent (no wait after an exponential)
+        auto pair_exp = [&](int b, int e) __attribute__((always_inline)) {
+            const int rq = e / 4, k = e % 4;
+            const float x0 = fmaf(sc[b][e], scale_log2, -L4[b][rq][k]);
+            const float x1 = fmaf(sc[b][e + 1], scale_log2, -L4[b][rq][k + 1]);
+            float p0 = __builtin_amdgcn_exp2f(x0), p1 = __builtin_amdgcn_exp2f(x1);
+            if (MASK) {
+                const int q = q0 + 32 * b + 8 * rq + 4 * g + k;  // rows q, q + 1
+                if (kw > q) p0 = 0.f;
+                if (kw > q + 1) p1 = 0.f;
+            }
+            pv[b][e] = p0;
+            pv[b][e + 1] = p1;
+        };
+        auto pair_grad = [&](int b, int e) __attribute__((always_inline)) {
+            tv[b][e] = pv[b][e] * dp[b][e];
+            tv[b][e + 1] = pv[b][e + 1] * dp[b][e + 1];
+            pp[b][e / 2] = pack_in<E>(pv[b][e], pv[b][e + 1]);
+            dd[b][e / 2] = pack_in<E>(tv[b][e], tv[b][e + 1]);
+        };
+
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) rd_dinit(0, rq);
+        static_for<LEAD>([&](auto ic) __attribute__((always_inline)) { rd(decltype(ic)::value); });
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<NP>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            mm(i);
+            if constexpr (i + LEAD < NP) rd(i + LEAD);
+            // the next tile's copies, during the first products
+            if constexpr (i >= 1 && i <= NCP) fetch_copy(qn, s ^ 1, i - 1);
+            static_for<NB>([&](auto bc) __attribute__((always_inline)) {
+                constexpr int b = decltype(bc)::value;
+                // block b's D, ten products ahead of its first dP product
+                if constexpr (b > 0 && i >= a_start(b) - 10 && i < a_start(b) - 6) rd_dinit(b, i - (a_start(b) - 10));
+                // each row group's statistics four products ahead of its elements
+                constexpr int e0 = v_start(b);
+                if constexpr (i >= e0 - 4 && i < e0 + 12 && (i - (e0 - 4)) % 4 == 0) rd_lse(b, (i - (e0 - 4)) / 4);
+                if constexpr (i >= e0 && i < e0 + 16) {
+                    if constexpr ((i - e0) % 2 == 0) pair_exp(b, i - e0);
+                    else pair_grad(b, i - e0 - 1);
+                }
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    auto step = [&](int qt, int s) __attribute__((always_inline)) {
+        // (past the last tile the copy repeats this one into the idle stage, so
+        // every step issues the same copies and no branch splits the step)
+        const int qn = qt + 1 < n_qt ? qt + 1 : qt;
+        fetch_stats(qn);
+        if (CAUSAL && qt * BQ < k0 + BKC)  // the tile reaches this workgroup's keys: mask
+            step_pipe(qt, s, qn, std::true_type{});
+        else
+            step_pipe(qt, s, qn, std::false_type{});
+        // the next tile's copies and statistics have landed: publish them
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        put_stats(s ^ 1);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    for (int qt = qt_begin; qt < n_qt; ++qt) step(qt, (qt - qt_begin) & 1);
+
+    // the accumulators were last written by matrix products the compiler does
+    // not see (mfma_acc): give them their result latency before any read
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    if (kw < Nk) {
+        // dK = scale * dK^T (accumulated negated), dV = dV^T: lane = key,
+        // register r -> head dim 32db + 8*(r/4) + 4*g + r%4
+        const int64_t row = k_head + (int64_t)kw * D;
+        const float nscale = -scale;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int col = db * 32 + 8 * rq + 4 * g;
+                store4<E>(dK, row + col, dkT[db][4 * rq] * nscale, dkT[db][4 * rq + 1] * nscale,
+                          dkT[db][4 * rq + 2] * nscale, dkT[db][4 * rq + 3] * nscale);
+                store4<E>(dV, row + col, dvT[db][4 * rq], dvT[db][4 * rq + 1], dvT[db][4 * rq + 2],
+                          dvT[db][4 * rq + 3]);
+            }
+    }
+}
+
 // ---------------------------------------------------------------- 2. dQ
 template <int D, int BC, int E, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q, const void *__restrict__ K,
@@ -616,6 +938,15 @@ static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
     const bool drop = a.drop.t > 0;
     if (stage < 0 || stage == 1) {
         const int n_kt = (a.Nk + 127) / 128;
+        if constexpr (D == 128 && E != ELT_F32 && FA_DKDV_KV) {
+            if (!drop) {
+                hipLaunchKernelGGL((bwd_dkdv_kv_kernel<E, CAUSAL>), dim3(BH * n_kt), dim3(256), 0, st, a.Q, a.K, a.V,
+                                   a.dO, a.LSE, a.Dvec, a.dK, a.dV, BH, a.Nq, a.Nk, a.scale, sl2, n_kt);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                goto dq;
+            }
+        }
         if (drop)
             hipLaunchKernelGGL((bwd_dkdv_kernel<D, E, CAUSAL, true>), dim3(BH * n_kt), dim3(512), 0, st, a.Q, a.K, a.V,
                                a.dO, a.LSE, a.Dvec, a.dK, a.dV, BH, a.Nq, a.Nk, a.scale, sl2, n_kt, a.drop);
@@ -625,6 +956,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+dq:
     if (stage < 0 || stage == 2) {
         const int n_qt = (a.Nq + 255) / 256;
         constexpr int BC = dq_keys<D, E>();
@@ -661,7 +993,9 @@ hipError_t launch_bwd(const BwdArgs &a, int stage) {
 const char *describe_bwd() {
     return "bwd_pre_kernel (D=rowsum(dO*O)) -> bwd_dkdv_kernel<D, 8 waves = 4 key groups x 2 query halves, "
            "128 keys, 64-row query steps (128 at d=64), "
-           "double-buffered Q/dO, transposed LDS reads> -> bwd_dq_kernel<D, 8 waves x 32 rows, 64-key tiles (128 at d=64)>; "
+           "double-buffered Q/dO, transposed LDS reads> (d=128 16-bit without dropout: bwd_dkdv_kv_kernel<4 waves, "
+           "one per SIMD, 32 keys each with K/V fragments in registers, dV/dK accumulators in AGPRs, 64-row steps "
+           "as a fixed product/softmax program>) -> bwd_dq_kernel<D, 8 waves x 32 rows, 64-key tiles (128 at d=64)>; "
            "no atomics";
 }
 

@@ -12,6 +12,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "fa_types.hpp"
 
 namespace fa {
@@ -48,6 +51,19 @@ template <int E>
 __device__ __forceinline__ f32x16_t mfma_in(u32x4_t a, u32x4_t b, f32x16_t c) {
     if constexpr (E == ELT_F16) return mfma_f16(a, b, c);
     else return mfma_bf16(a, b, c);
+}
+
+// acc += A B with the accumulator pinned to accumulation registers (AGPRs),
+// for accumulators that only ever feed matrix products.  The compiler does not
+// see the product's latency, so a reader of acc outside these products must
+// wait for it (the callers put the wait states in front of such reads), and
+// the B operand must have been written at least two instructions earlier.
+template <int E>
+__device__ __forceinline__ void mfma_acc(f32x16_t &acc, u32x4_t a, u32x4_t b) {
+    if constexpr (E == ELT_F16)
+        asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // Round-to-nearest-even packing of two floats (low half = a).
@@ -174,6 +190,17 @@ __device__ __forceinline__ u32x4_t tr_operand(const uint16_t *T, int r0, int m0,
     const u32x2_t a = ds_read_tr16(T + tile_off<W>(row, col));
     const u32x2_t b = ds_read_tr16(T + tile_off<W>(row + 8, col));
     return u32x4_t{a[0], a[1], b[0], b[1]};
+}
+
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N - 1>{}),
+// in order: a loop whose index is a compile-time constant in every copy.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // An empty statement with a side effect: placed in a rarely taken uniform
