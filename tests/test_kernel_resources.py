@@ -8,8 +8,7 @@ and 128, causal or not) must keep all its values in registers: a ScratchSize
 above 0 means spilled registers going through memory on every step.  The
 float32 and dropout variants are reported, not held to it (their spills are
 stated with the kernel notes of the library's design record).  The dK/dV
-pass that keeps K and V in registers runs one wave per SIMD and may use the
-whole register file."""
+and dQ passes that run one wave per SIMD may use the whole register file."""
 import os
 import re
 import shutil
@@ -53,7 +52,7 @@ def _hot(name):
         return a[3] != 2 and a[6] == 0
     if "bwd_dkdv_kernel" in name:  # <D, E, CAUSAL, DROP>
         return a[1] != 2 and a[3] == 0
-    if "bwd_dkdv_kv_kernel" in name:  # <E, CAUSAL>: d = 128, 16-bit, no dropout only
+    if "bwd_dkdv_kv_kernel" in name or "bwd_dq_kv_kernel" in name:  # <E, CAUSAL>: d = 128, 16-bit, no dropout only
         return True
     if "bwd_dq_kernel" in name:  # <D, BC, E, CAUSAL, DROP>
         return a[2] != 2 and a[4] == 0
@@ -74,7 +73,7 @@ def reports():
 
 def test_every_kernel_reported(reports):
     names = ("fwd_kernel", "fwd_merge_kernel", "v_pack_kernel", "bwd_pre_kernel", "bwd_dkdv_kernel",
-             "bwd_dkdv_kv_kernel", "bwd_dq_kernel")
+             "bwd_dkdv_kv_kernel", "bwd_dq_kernel", "bwd_dq_kv_kernel")
     kinds = {k for n in reports for k in names if "_ZN2fa%d%s" % (len(k), k) in n}
     assert kinds == set(names), sorted(reports)
 
@@ -88,12 +87,12 @@ def test_hot_path_does_not_spill(reports):
                                                         "" if _hot(n) else "  (not held)"))
     assert not spilling, spilling
     for n, r in hot.items():
-        if "bwd_dkdv_kv_kernel" in n:
-            # one wave per SIMD: the whole register file, 256 of each kind; without
-            # the causal mask's second program the AGPRs hold exactly the 128 dV/dK
-            # accumulators (no VGPR spilled into them)
+        if "bwd_dkdv_kv_kernel" in n or "bwd_dq_kv_kernel" in n:
+            # one wave per SIMD: the whole register file, 256 of each kind; the
+            # dK/dV pass's AGPRs hold exactly its 128 accumulators (no VGPR
+            # spilled into them)
             assert r["vgpr"] <= 256 and r["agpr"] <= 256, (n, r)
-            if _demangled_args(n)[1] == 0:
+            if "bwd_dkdv_kv_kernel" in n:
                 assert r["agpr"] == 128, (n, r)
         else:
             assert r["vgpr"] + r["agpr"] <= 256, (n, r)  # two waves per SIMD

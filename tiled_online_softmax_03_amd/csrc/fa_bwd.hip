@@ -26,7 +26,10 @@
 //   2. bwd_dq_kernel    Q-stationary: a workgroup owns 256 query rows (32 per
 //                       wave, Q and dO rows held in VGPRs) and streams K/V
 //                       tiles like the forward: S^T = K Q^T, dP^T = V dO^T,
-//                       dS^T, dQ^T += K^T dS^T.
+//                       dS^T, dQ^T += K^T dS^T.  For d = 128 16-bit data
+//                       without dropout, bwd_dq_kv_kernel: four waves, one per
+//                       SIMD, 64 rows each, so every K/V fragment read from
+//                       LDS feeds two products.
 // dQ, dK and dV are therefore deterministic.  The price is that S and dP are
 // formed twice (7 matrix products instead of 5).
 //
@@ -48,6 +51,11 @@
 // (bwd_dkdv_kv_kernel); 0 selects the two-waves-per-SIMD pass for it too.
 #ifndef FA_DKDV_KV
 #define FA_DKDV_KV 1
+#endif
+// The d = 128 16-bit dQ pass without dropout takes 64 query rows per wave
+// (bwd_dq_kv_kernel); 0 selects the two-waves-per-SIMD pass for it too.
+#ifndef FA_DQ_KV
+#define FA_DQ_KV 1
 #endif
 
 namespace fa {
@@ -495,6 +503,7 @@ void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, 
     const int kw0 = k0 + wave * 32;  // first key of this wave
     const int kw = kw0 + l32;        // this lane's key
     const int kw_ld = kw < Nk ? kw : Nk - 1;  // keys past Nk compute on a real row and are never stored
+    const int kwg = kw - 4 * g;  // the key less the lane's 4g offset in the score registers' row order
 
     const int n_qt = (Nq + BQ - 1) / BQ;
     const int qt_begin = CAUSAL ? min(k0 / BQ, n_qt) : 0;  // earlier rows see none of these keys
@@ -655,10 +664,10 @@ void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, 
             const float x0 = fmaf(sc[b][e], scale_log2, -L4[b][rq][k]);
             const float x1 = fmaf(sc[b][e + 1], scale_log2, -L4[b][rq][k + 1]);
             float p0 = __builtin_amdgcn_exp2f(x0), p1 = __builtin_amdgcn_exp2f(x1);
-            if (MASK) {
-                const int q = q0 + 32 * b + 8 * rq + 4 * g + k;  // rows q, q + 1
-                if (kw > q) p0 = 0.f;
-                if (kw > q + 1) p1 = 0.f;
+            if (MASK) {  // rows q0 + c + 4g and the next one against this lane's key
+                const int c = 32 * b + 8 * rq + k;
+                if (kwg > q0 + c) p0 = 0.f;
+                if (kwg > q0 + c + 1) p1 = 0.f;
             }
             pv[b][e] = p0;
             pv[b][e + 1] = p1;
@@ -696,15 +705,13 @@ void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, 
         });
     };
 
-    auto step = [&](int qt, int s) __attribute__((always_inline)) {
+    auto step = [&](int qt, auto mask_c) __attribute__((always_inline)) {
+        const int s = (qt - qt_begin) & 1;
         // (past the last tile the copy repeats this one into the idle stage, so
         // every step issues the same copies and no branch splits the step)
         const int qn = qt + 1 < n_qt ? qt + 1 : qt;
         fetch_stats(qn);
-        if (CAUSAL && qt * BQ < k0 + BKC)  // the tile reaches this workgroup's keys: mask
-            step_pipe(qt, s, qn, std::true_type{});
-        else
-            step_pipe(qt, s, qn, std::false_type{});
+        step_pipe(qt, s, qn, mask_c);
         // the next tile's copies and statistics have landed: publish them
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         put_stats(s ^ 1);
@@ -712,7 +719,12 @@ void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, 
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
-    for (int qt = qt_begin; qt < n_qt; ++qt) step(qt, (qt - qt_begin) & 1);
+    // Causal: the first tiles reach this workgroup's keys and take the masked
+    // program, in a loop of their own (one loop holding both programs needs
+    // more registers than the file has); the rest need no mask.
+    const int qt_mask_end = CAUSAL ? min(n_qt, (k0 + BKC + BQ - 1) / BQ) : qt_begin;
+    for (int qt = qt_begin; qt < qt_mask_end; ++qt) step(qt, std::true_type{});
+    for (int qt = qt_mask_end; qt < n_qt; ++qt) step(qt, std::false_type{});
 
     // the accumulators were last written by matrix products the compiler does
     // not see (mfma_acc): give them their result latency before any read
@@ -917,6 +929,296 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
     }
 }
 
+// ---------------------------------------------------------------- 2'. dQ with 64 query rows per wave
+// The d = 128 16-bit pass without dropout.  Four waves, one per SIMD, each
+// owning 64 query rows (two 32-row blocks) of the workgroup's 256: every K and
+// V fragment read from LDS feeds the products of both blocks, which halves
+// the LDS reads per product of the two-waves-per-SIMD pass above.  Q^T and
+// dO^T fragments stay in registers, dQ^T accumulates in AGPRs (mfma_acc),
+// S^T and dP^T land in VGPRs where the softmax gradient reads them.  K/V
+// tiles of 64 keys are double-buffered in LDS, copied global -> LDS by inline
+// assembly and waited for once per step, before the barrier (the compiler
+// uses no M0 of its own here).  A step is two 32-key blocks, each 32 S/dP
+// products (A) and 16 dQ products (B), ordered A0 A1 B0 B1: block 0's
+// softmax gradient runs beside A1, block 1's beside B0 and the first half of
+// B1 (B1's first eight products need only keys 0..15 of the block).
+template <int E, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, const void *__restrict__ V,
+                      const void *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Dvec,
+                      void *__restrict__ dQ, int BH, int Nq, int Nk, float scale, float scale_log2, int n_qt) {
+    constexpr int D = 128, NW = 4, BR = 64 * NW, BC = 64;
+    constexpr int NKS = D / 16;       // k-steps over the head dim
+    constexpr int NDB = D / 32;       // 32-column blocks of dQ^T
+    constexpr int TILE = BC * D * 2;  // bytes of one K (or V) tile
+    constexpr int NCP = BC / 16;      // 1 KiB copies per wave per tensor per tile
+    constexpr int NP = 96;            // matrix products per step
+    constexpr int LEAD = FA_KV_LEAD, NSLOT = LEAD + 1;
+    static_assert(E != ELT_F32, "16-bit operands are copied global -> LDS as they are");
+    // stage s: K at 2 s TILE, V at (2 s + 1) TILE
+    __shared__ __attribute__((aligned(16))) unsigned char lds[4 * TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, g = lane >> 5;
+
+    int bh, qt;
+    if constexpr (CAUSAL) {
+        const int L = blockIdx.x;  // longest rows first
+        qt = n_qt - 1 - L / BH;
+        bh = L % BH;
+    } else {
+        const int L = xcd_remap(blockIdx.x, gridDim.x);
+        bh = L / n_qt;
+        qt = L % n_qt;
+    }
+    const int64_t q_head = (int64_t)bh * Nq * D;
+    const int64_t k_head = (int64_t)bh * Nk * D;
+    const int q_w0 = qt * BR + 64 * wave;  // first row of this wave
+
+    int k_end = Nk;
+    if constexpr (CAUSAL) k_end = min(Nk, min(qt * BR + BR, Nq));
+    const int n_kt = (k_end + BC - 1) / BC;
+
+    // Q^T and dO^T fragments of both row blocks (B operands, k = head-dim index
+    // 16*ks + 8*g + v, lane = row q_w0 + 32 r + l32) and the rows' statistics.
+    u32x4_t qf[2][NKS], df[2][NKS];
+    float lse2[2], dv[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int q = q_w0 + 32 * r + l32;
+        const int q_ld = q < Nq ? q : Nq - 1;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            qf[r][ks] = load8_operand<E>(Q, q_head + (int64_t)q_ld * D + 16 * ks + 8 * g);
+            df[r][ks] = load8_operand<E>(dO, q_head + (int64_t)q_ld * D + 16 * ks + 8 * g);
+        }
+        lse2[r] = LSE[(int64_t)bh * Nq + q_ld] * kLog2e;
+        dv[r] = Dvec[(int64_t)bh * Nq + q_ld];
+    }
+    // last key each lane's rows see (past Nk, or causal past the row), less
+    // the lane's 4g offset in the score registers' key order
+    int klim[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) klim[r] = (CAUSAL ? min(q_w0 + 32 * r + l32, Nk - 1) : Nk - 1) - 4 * g;
+
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            qf[r][ks] = to_agpr(qf[r][ks]);
+        }
+
+    // Per-lane LDS byte offsets in a tile (tile_off<128> layout):
+    //  a_off[ks]: the A operand (key row l32 of a 32-key block, head dims
+    //  16ks + 8g .. +7); t_off[db][hf]: the transposed read of key rows
+    //  4g + j/4 + 8 hf, head dims 32 db + 16 ((lane / 16) % 2) + 4 (j % 4).
+    uint32_t a_off[NKS], t_off[NDB][2];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) a_off[ks] = 2u * (uint32_t)tile_off<D>(l32, 16 * ks + 8 * g);
+    {
+        const int j = lane & 15;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                t_off[db][hf] = 2u * (uint32_t)tile_off<D>(4 * g + (j >> 2) + 8 * hf, 32 * db + 16 * ((lane >> 4) & 1) + 4 * (j & 3));
+    }
+
+    // Copies of a tile: blocks of 4 key rows (1 KiB), NCP per wave per tensor,
+    // block b = wave + 4 jb (the same swizzle for every jb); rows past Nk
+    // re-read row Nk - 1 (their scores are masked).
+    const uint16_t *Kh = static_cast<const uint16_t *>(K) + k_head;
+    const uint16_t *Vh = static_cast<const uint16_t *>(V) + k_head;
+    const int cp_row = wave * 4 + lane / 16;  // + 16 jb
+    const uint32_t cp_col = (uint32_t)((lane & 15) ^ swz<D>(cp_row)) * 16u;
+    auto fetch_copy = [&](int kt, int s, int jb) __attribute__((always_inline)) {
+        const int grow = min(kt * BC + cp_row + 16 * jb, Nk - 1);
+        const uint32_t off = (uint32_t)grow * (uint32_t)(D * 2) + cp_col;  // bytes from the head's first row
+        const uint32_t dk = (uint32_t)(2 * s * TILE + (wave + NW * jb) * 1024);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 in the clobber list: see the kernel's notes
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(Kh), "s"(dk)
+                     : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(Vh),
+                     "s"(dk + (uint32_t)TILE)
+                     : "memory", "m0");
+#pragma clang diagnostic pop
+    };
+
+    f32x16_t dqT[2][NDB];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dqT[r][db] = f32x16_t{};
+
+    if (n_kt > 0) {
+#pragma unroll
+        for (int jb = 0; jb < NCP; ++jb) fetch_copy(0, 0, jb);
+    }
+    wait_vmem();
+    __syncthreads();
+    asm volatile("s_nop 3" ::: "memory");  // the zeroed accumulators, before mfma_acc reads them
+
+    // One key tile in stage s: products 0..31 A(block 0), 32..63 A(block 1),
+    // 64..79 B(block 0), 80..95 B(block 1).  A product i < 64: k-step ks =
+    // (i % 32) / 4, tensor w = (i % 4) / 2 (K: S^T, V: dP^T), row block i % 2.
+    // B product j = (i - 64) % 16: k-step h = j / 8, db = (j % 8) / 2, row block j % 2.
+    // MASK: apply the mask of keys past Nk and, causal, of keys after the row.
+    auto step_pipe = [&](int kt, int s, int kn, auto mask_c) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_c)::value;
+        const uint32_t sb = (uint32_t)(2 * s * TILE);
+        uint32_t ao[NKS], to[NDB][2];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) ao[ks] = a_off[ks] + sb;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) { to[db][0] = t_off[db][0] + sb; to[db][1] = t_off[db][1] + sb; }
+        const int k0 = kt * BC;
+        u32x4_t opr[NSLOT];
+        f32x16_t sc[2][2], dp[2][2];  // [key block][row block]
+        float pv[2][2][16];
+        uint32_t dd[2][2][8];
+        // Product i is issued in slot n; its operand goes through ring entry
+        // (n / 2) % NSLOT.  An A product's operand is shared by the two row
+        // blocks (products i, i + 1, i even): read once.
+        auto rd = [&](int n, int i) __attribute__((always_inline)) {
+            if (i < 64) {
+                if (i % 2 == 0) {
+                    const int kb = i / 32, ks = (i % 32) / 4, w = (i % 4) / 2;
+                    opr[(n / 2) % NSLOT] = *reinterpret_cast<const u32x4_t *>(lds + ao[ks] + w * TILE + kb * 32 * 256);
+                }
+            } else {
+                const int kb = (i - 64) / 16, j = (i - 64) % 16, h = j / 8, db = (j % 8) / 2;
+                if (j % 2 == 0) {
+                    const unsigned off = (kb * 32 + 16 * h) * 256;
+                    const u32x2_t x0 = ds_read_tr16(reinterpret_cast<const uint16_t *>(lds + to[db][0] + off));
+                    const u32x2_t x1 = ds_read_tr16(reinterpret_cast<const uint16_t *>(lds + to[db][1] + off));
+                    opr[(n / 2) % NSLOT] = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
+                }
+            }
+        };
+        auto mm = [&](int n, int i) __attribute__((always_inline)) {
+            const u32x4_t a = opr[(n / 2) % NSLOT];
+            if (i < 64) {
+                const int kb = i / 32, ks = (i % 32) / 4, w = (i % 4) / 2, r = i % 2;
+                if (w == 0) {  // S^T: Q^T from AGPRs
+                    if (ks == 0) sc[kb][r] = mfma_bagpr_first<E>(a, qf[r][ks]);
+                    else mfma_bagpr<E>(sc[kb][r], a, qf[r][ks]);
+                } else {  // dP^T: dO^T from VGPRs
+                    dp[kb][r] = mfma_in<E>(a, df[r][ks], ks == 0 ? f32x16_t{} : dp[kb][r]);
+                }
+            } else {
+                const int kb = (i - 64) / 16, j = (i - 64) % 16, h = j / 8, db = (j % 8) / 2, r = j % 2;
+                mfma_acc<E>(dqT[r][db], a, u32x4_t{dd[kb][r][4 * h], dd[kb][r][4 * h + 1], dd[kb][r][4 * h + 2], dd[kb][r][4 * h + 3]});
+            }
+        };
+        // elements e, e + 1 (register pair) of key block kb, row block r:
+        // P = exp2(s c - LSE log2 e), dS = P (dP - D), in two halves
+        auto pair_exp = [&](int kb, int r, int e) __attribute__((always_inline)) {
+            float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r][e], scale_log2, -lse2[r]));
+            float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r][e + 1], scale_log2, -lse2[r]));
+            if (MASK) {  // keys k0 + c + 4g and the next one against the row's last key
+                const int c = 32 * kb + 8 * (e / 4) + (e % 4);
+                if (k0 + c > klim[r]) p0 = 0.f;
+                if (k0 + c + 1 > klim[r]) p1 = 0.f;
+            }
+            pv[kb][r][e] = p0;
+            pv[kb][r][e + 1] = p1;
+        };
+        auto pair_grad = [&](int kb, int r, int e) __attribute__((always_inline)) {
+            const float t0 = pv[kb][r][e] * (dp[kb][r][e] - dv[r]);
+            const float t1 = pv[kb][r][e + 1] * (dp[kb][r][e + 1] - dv[r]);
+            dd[kb][r][e / 2] = pack_in<E>(t0, t1);
+        };
+        // the 16 pairs of a key block (8 per row block), in the order the B
+        // products need them: keys 0..15 of both row blocks first
+        auto vwork = [&](int kb, int u) __attribute__((always_inline)) {  // u = 0..31
+            const int pr = u / 2, half = u % 2;             // pair pr = 0..15
+            const int h = pr / 8, r = (pr / 4) % 2, e = 8 * h + 2 * (pr % 4);
+            if (half == 0) pair_exp(kb, r, e);
+            else pair_grad(kb, r, e);
+        };
+
+        // Slot n issues product perm(n).  The masked program (the ragged or
+        // diagonal tile, one per row tile at most) runs A0 B0 A1 B1 with each
+        // softmax gradient between its A and B groups: fewer values live at
+        // once than with the overlap, which the extra mask arithmetic needs.
+        auto perm = [](int n) constexpr {
+            if (!MASK) return n;
+            return n < 32 ? n : n < 48 ? n + 32 : n < 80 ? n - 16 : n;
+        };
+        static_for<LEAD>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int n = 2 * decltype(ic)::value;
+            rd(n, perm(n));
+            rd(n + 1, perm(n + 1));
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<NP>([&](auto nc) __attribute__((always_inline)) {
+            constexpr int n = decltype(nc)::value;
+            if constexpr (MASK && (n == 32 || n == 80)) {
+                // the whole softmax gradient of the key block whose S/dP products
+                // just finished, after their result latency (mfma_bagpr)
+                asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+                static_for<32>([&](auto uc) __attribute__((always_inline)) { vwork(n == 32 ? 0 : 1, decltype(uc)::value); });
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            mm(n, perm(n));
+            if constexpr (n % 2 == 1 && (n + 1) / 2 + LEAD - 1 < NP / 2) {
+                constexpr int m = n + 1 + 2 * (LEAD - 1);  // the pair LEAD pairs ahead
+                rd(m, perm(m));
+                rd(m + 1, perm(m + 1));
+            }
+            if constexpr (n >= 1 && n <= NCP) fetch_copy(kn, s ^ 1, n - 1);
+            if constexpr (!MASK) {
+                // block 0's softmax beside A(block 1) (32 units in 32 slots);
+                // block 1's beside B(block 0) and the first half of B(block 1):
+                // 32 units in 24 slots, two per slot in the first eight
+                if constexpr (n >= 33 && n < 65) vwork(0, n - 33);
+                if constexpr (n >= 65 && n < 73) {
+                    vwork(1, 2 * (n - 65));
+                    vwork(1, 2 * (n - 65) + 1);
+                }
+                if constexpr (n >= 73 && n < 89) vwork(1, n - 73 + 16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    auto step = [&](int kt, auto mask_c) __attribute__((always_inline)) {
+        const int kn = kt + 1 < n_kt ? kt + 1 : kt;
+        step_pipe(kt, kt & 1, kn, mask_c);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // Tiles that need no mask come first: every key exists and, causal, every
+    // key precedes the workgroup's first row.  The rest take the masked program
+    // in a loop of their own (one loop holding both programs needs more
+    // registers than the file has).
+    int n_full = Nk / BC;
+    if constexpr (CAUSAL) n_full = min(n_full, (qt * BR + 1) / BC);
+    n_full = min(n_full, n_kt);
+    for (int kt = 0; kt < n_full; ++kt) step(kt, std::false_type{});
+    for (int kt = n_full; kt < n_kt; ++kt) step(kt, std::true_type{});
+
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");  // mfma_acc results, before they are read
+    // dQ = scale * (dQ^T)^T: lane = row, register r -> head dim 32db + 8*(r/4) + 4*g + r%4
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int q = q_w0 + 32 * r + l32;
+        if (q < Nq) {
+            const int64_t row = q_head + (int64_t)q * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq)
+                    store4<E>(dQ, row + db * 32 + 8 * rq + 4 * g, dqT[r][db][4 * rq] * scale,
+                              dqT[r][db][4 * rq + 1] * scale, dqT[r][db][4 * rq + 2] * scale,
+                              dqT[r][db][4 * rq + 3] * scale);
+        }
+    }
+}
+
 // Keys per tile of the dQ pass: at d = 64 a tile carries half the matrix work
 // of d = 128, so it takes twice the keys (the 32-key blocks inside keep the
 // registers the same).
@@ -959,6 +1261,13 @@ static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
 dq:
     if (stage < 0 || stage == 2) {
         const int n_qt = (a.Nq + 255) / 256;
+        if constexpr (D == 128 && E != ELT_F32 && FA_DQ_KV) {
+            if (!drop) {
+                hipLaunchKernelGGL((bwd_dq_kv_kernel<E, CAUSAL>), dim3(BH * n_qt), dim3(256), 0, st, a.Q, a.K, a.V, a.dO,
+                                   a.LSE, a.Dvec, a.dQ, BH, a.Nq, a.Nk, a.scale, sl2, n_qt);
+                return hipGetLastError();
+            }
+        }
         constexpr int BC = dq_keys<D, E>();
         if (drop)
             hipLaunchKernelGGL((bwd_dq_kernel<D, BC, E, CAUSAL, true>), dim3(BH * n_qt), dim3(512), 0, st, a.Q, a.K, a.V,
@@ -995,8 +1304,9 @@ const char *describe_bwd() {
            "128 keys, 64-row query steps (128 at d=64), "
            "double-buffered Q/dO, transposed LDS reads> (d=128 16-bit without dropout: bwd_dkdv_kv_kernel<4 waves, "
            "one per SIMD, 32 keys each with K/V fragments in registers, dV/dK accumulators in AGPRs, 64-row steps "
-           "as a fixed product/softmax program>) -> bwd_dq_kernel<D, 8 waves x 32 rows, 64-key tiles (128 at d=64)>; "
-           "no atomics";
+           "as a fixed product/softmax program>) -> bwd_dq_kernel<D, 8 waves x 32 rows, 64-key tiles (128 at d=64)> "
+           "(d=128 16-bit without dropout: bwd_dq_kv_kernel<4 waves, one per SIMD, 64 rows each, Q^T in AGPRs, "
+           "dQ accumulators in AGPRs, 64-key tiles as a fixed program>); no atomics";
 }
 
 }  // namespace fa

@@ -66,6 +66,38 @@ __device__ __forceinline__ void mfma_acc(f32x16_t &acc, u32x4_t a, u32x4_t b) {
         asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// acc (+)= A B with the B operand held in AGPRs (a fragment that only feeds
+// matrix products) and the accumulator in VGPRs, where vector code reads it.
+// As for mfma_acc, the compiler does not see the latency: a vector read of
+// acc must come several products later (the callers' schedules place it at
+// least two products after the last write).
+template <int E>
+__device__ __forceinline__ void mfma_bagpr(f32x16_t &acc, u32x4_t a, u32x4_t b) {
+    if constexpr (E == ELT_F16)
+        asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+    else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+// A fragment moved to AGPRs once, where mfma_bagpr reads it (the compiler
+// would otherwise keep it in VGPRs and copy it over before every product).
+__device__ __forceinline__ u32x4_t to_agpr(u32x4_t v) {
+    uint32_t x0, x1, x2, x3;
+    asm("v_accvgpr_write_b32 %0, %1" : "=a"(x0) : "v"(v[0]));
+    asm("v_accvgpr_write_b32 %0, %1" : "=a"(x1) : "v"(v[1]));
+    asm("v_accvgpr_write_b32 %0, %1" : "=a"(x2) : "v"(v[2]));
+    asm("v_accvgpr_write_b32 %0, %1" : "=a"(x3) : "v"(v[3]));
+    return u32x4_t{x0, x1, x2, x3};
+}
+template <int E>
+__device__ __forceinline__ f32x16_t mfma_bagpr_first(u32x4_t a, u32x4_t b) {  // acc = A B
+    f32x16_t d;
+    if constexpr (E == ELT_F16)
+        asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+    else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+    return d;
+}
+
 // Round-to-nearest-even packing of two floats (low half = a).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     f32x2_t x = {a, b};
