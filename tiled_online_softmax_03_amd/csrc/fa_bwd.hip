@@ -591,7 +591,7 @@ void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, 
     }
     wait_vmem();
     __syncthreads();
-    asm volatile("s_nop 3" ::: "memory");  // the zeroed accumulators, before mfma_acc reads them
+    mfma_wait<3>();  // the zeroed accumulators, before mfma_acc reads them
 
     // Position of group G (16 products) in the step's order A0 A1 B0 A2 B1 ... B(NB-1):
     // is it an A group, and of which block.
@@ -728,7 +728,7 @@ void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, 
 
     // the accumulators were last written by matrix products the compiler does
     // not see (mfma_acc): give them their result latency before any read
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    mfma_drain();
     if (kw < Nk) {
         // dK = scale * dK^T (accumulated negated), dV = dV^T: lane = key,
         // register r -> head dim 32db + 8*(r/4) + 4*g + r%4
@@ -1058,7 +1058,7 @@ void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, co
     }
     wait_vmem();
     __syncthreads();
-    asm volatile("s_nop 3" ::: "memory");  // the zeroed accumulators, before mfma_acc reads them
+    mfma_wait<3>();  // the zeroed accumulators, before mfma_acc reads them
 
     // One key tile in stage s: products 0..31 A(block 0), 32..63 A(block 1),
     // 64..79 B(block 0), 80..95 B(block 1).  A product i < 64: k-step ks =
@@ -1158,7 +1158,7 @@ void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, co
             if constexpr (MASK && (n == 32 || n == 80)) {
                 // the whole softmax gradient of the key block whose S/dP products
                 // just finished, after their result latency (mfma_bagpr)
-                asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+                mfma_drain();
                 static_for<32>([&](auto uc) __attribute__((always_inline)) { vwork(n == 32 ? 0 : 1, decltype(uc)::value); });
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -1173,6 +1173,9 @@ void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, co
                 // block 0's softmax beside A(block 1) (32 units in 32 slots);
                 // block 1's beside B(block 0) and the first half of B(block 1):
                 // 32 units in 24 slots, two per slot in the first eight
+                // (the first reads of a key block's scores wait for the result
+                // latency of its last S^T products, which the compiler does not see)
+                if constexpr (n == 33 || n == 65) mfma_wait<7>();
                 if constexpr (n >= 33 && n < 65) vwork(0, n - 33);
                 if constexpr (n >= 65 && n < 73) {
                     vwork(1, 2 * (n - 65));
@@ -1201,7 +1204,7 @@ void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, co
     for (int kt = 0; kt < n_full; ++kt) step(kt, std::false_type{});
     for (int kt = n_full; kt < n_kt; ++kt) step(kt, std::true_type{});
 
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");  // mfma_acc results, before they are read
+    mfma_drain();  // mfma_acc results, before they are read
     // dQ = scale * (dQ^T)^T: lane = row, register r -> head dim 32db + 8*(r/4) + 4*g + r%4
 #pragma unroll
     for (int r = 0; r < 2; ++r) {

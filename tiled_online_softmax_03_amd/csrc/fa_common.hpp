@@ -66,6 +66,25 @@ __device__ __forceinline__ void mfma_acc(f32x16_t &acc, u32x4_t a, u32x4_t b) {
         asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// Wait states for the result of matrix products the compiler does not see
+// (mfma_acc, mfma_bagpr) before vector code reads or overwrites their
+// registers: a 16-pass product needs 19 on this family, 32 leaves margin.
+// (The scheduling barriers keep vector code from being moved above the wait:
+// the asm only orders memory operations.)
+__device__ __forceinline__ void mfma_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+// A shorter wait (n + 1 wait states, n = 0..7) for the same purpose, where the
+// schedule already places other instructions in between.
+template <int N>
+__device__ __forceinline__ void mfma_wait() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop %0" ::"n"(N) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // acc (+)= A B with the B operand held in AGPRs (a fragment that only feeds
 // matrix products) and the accumulator in VGPRs, where vector code reads it.
 // As for mfma_acc, the compiler does not see the latency: a vector read of
@@ -78,6 +97,25 @@ __device__ __forceinline__ void mfma_bagpr(f32x16_t &acc, u32x4_t a, u32x4_t b) 
     else
         asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
 }
+// 16 bytes of global memory loaded straight into an AGPR tuple.  The load is
+// still in flight when this returns: wait_agpr_loads must run before anything
+// reads the result (it takes every such tuple as an operand, so no use can be
+// placed ahead of it).
+__device__ __forceinline__ u32x4_t load16_agpr(const void *p) {
+    u32x4_t v;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(v) : "v"(p) : "memory");
+    return v;
+}
+// Wait for the loads of load16_agpr into the 16 tuples of f[2][8].
+__device__ __forceinline__ void wait_agpr_loads(u32x4_t (&f)[2][8]) {
+    asm volatile("s_waitcnt vmcnt(0)"
+                 : "+a"(f[0][0]), "+a"(f[0][1]), "+a"(f[0][2]), "+a"(f[0][3]), "+a"(f[0][4]), "+a"(f[0][5]),
+                   "+a"(f[0][6]), "+a"(f[0][7]), "+a"(f[1][0]), "+a"(f[1][1]), "+a"(f[1][2]), "+a"(f[1][3]),
+                   "+a"(f[1][4]), "+a"(f[1][5]), "+a"(f[1][6]), "+a"(f[1][7])
+                 :
+                 : "memory");
+}
+
 // A fragment moved to AGPRs once, where mfma_bagpr reads it (the compiler
 // would otherwise keep it in VGPRs and copy it over before every product).
 __device__ __forceinline__ u32x4_t to_agpr(u32x4_t v) {
@@ -120,6 +158,15 @@ __device__ __forceinline__ float f16_lo(uint32_t u) {
 }
 __device__ __forceinline__ float f16_hi(uint32_t u) {
     return (float)__builtin_bit_cast(f16x2_t, u)[1];
+}
+
+// Largest of three floats in one v_max3_f32.  The scores it takes are never
+// NaN, so the quieting the compiler would add in front of fmaxf (the IEEE mode
+// treats signalling NaNs specially) is left out.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float d;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
 }
 
 // Both halves' value combined: lanes l and l^32 exchange through
