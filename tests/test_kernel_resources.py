@@ -52,7 +52,8 @@ def _hot(name):
         return a[3] != 2 and a[6] == 0
     if "bwd_dkdv_kernel" in name:  # <D, E, CAUSAL, DROP>
         return a[1] != 2 and a[3] == 0
-    if "bwd_dkdv_kv_kernel" in name or "bwd_dq_kv_kernel" in name:  # <E, CAUSAL>: d = 128, 16-bit, no dropout only
+    if "bwd_dkdv_kv_kernel" in name or "bwd_dq_kv_kernel" in name or "fwd_r64_kernel" in name:
+        # <E, CAUSAL>: d = 128, 16-bit, no dropout only
         return True
     if "bwd_dq_kernel" in name:  # <D, BC, E, CAUSAL, DROP>
         return a[2] != 2 and a[4] == 0
@@ -72,7 +73,7 @@ def reports():
 
 
 def test_every_kernel_reported(reports):
-    names = ("fwd_kernel", "fwd_merge_kernel", "v_pack_kernel", "bwd_pre_kernel", "bwd_dkdv_kernel",
+    names = ("fwd_kernel", "fwd_r64_kernel", "fwd_merge_kernel", "v_pack_kernel", "bwd_pre_kernel", "bwd_dkdv_kernel",
              "bwd_dkdv_kv_kernel", "bwd_dq_kernel", "bwd_dq_kv_kernel")
     kinds = {k for n in reports for k in names if "_ZN2fa%d%s" % (len(k), k) in n}
     assert kinds == set(names), sorted(reports)
@@ -87,7 +88,7 @@ def test_hot_path_does_not_spill(reports):
                                                         "" if _hot(n) else "  (not held)"))
     assert not spilling, spilling
     for n, r in hot.items():
-        if "bwd_dkdv_kv_kernel" in n or "bwd_dq_kv_kernel" in n:
+        if "bwd_dkdv_kv_kernel" in n or "bwd_dq_kv_kernel" in n or "fwd_r64_kernel" in n:
             # one wave per SIMD: the whole register file, 256 of each kind; the
             # dK/dV pass's AGPRs hold exactly its 128 accumulators (no VGPR
             # spilled into them)
