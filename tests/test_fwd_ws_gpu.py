@@ -108,3 +108,60 @@ def test_long_causal_equal_fa_fwd():
     O2, L2 = fa.forward(inp["Q"], inp["K"], inp["V"], w.scale, True)
     torch.cuda.synchronize()
     assert torch.equal(O, O2) and torch.equal(LSE, L2)
+
+
+def _rising(B, H, Nq, Nk, d, dtype, step_log2, seed):
+    """Q rows of ones (times a per-row factor in [0.5, 1.36]), key j a multiple
+    a_j of ones with a_j rising along the keys, so that the scaled score of key
+    j, in log2 units, grows by about `step_log2` per key (times the row
+    factor): every 64-key tile raises each row's maximum well past the
+    rescale threshold of 8, and the reference maximum moves on every tile."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    td = DT[dtype]
+    scale = 1.0 / math.sqrt(d)
+    unit = d * scale * math.log2(math.e)  # log2-scaled score of ones . ones
+    rows = 0.5 + (torch.arange(Nq, device="cuda", dtype=torch.float32) % 7) / 7.0
+    a = step_log2 * torch.arange(Nk, device="cuda", dtype=torch.float32) / unit
+    Q = (rows[:, None] * torch.ones(d, device="cuda")).expand(B, H, Nq, d).to(td).contiguous()
+    K = (a[:, None] * torch.ones(d, device="cuda")).expand(B, H, Nk, d).to(td).contiguous()
+    V = torch.randn((B, H, Nk, d), generator=g, device="cuda").to(td).contiguous()
+    return {"Q": Q, "K": K, "V": V}, scale
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rescale_every_tile(causal, dtype):
+    """The maximum rises on every key tile, so the d = 128 key loop's rescale
+    branch (which recomputes the first 32 keys' exponentials after the vote)
+    runs on every step: still fa_fwd's bits, and the oracle's values."""
+    Nq, Nk = (700, 700) if causal else (300, 1000)
+    inp, scale = _rising(1, 2, Nq, Nk, 128, dtype, 0.2, 77)
+    say("fwd_ws rescale every tile", dtype, causal)
+    O, LSE = _ws_fwd(inp, scale, causal)
+    O2, L2 = fa.forward(inp["Q"], inp["K"], inp["V"], scale, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2) and torch.equal(LSE, L2)
+    q, k, v = oracle_view(inp["Q"]), oracle_view(inp["K"]), oracle_view(inp["V"])
+    O_ref, LSE_ref = oracle.fwd(q, k, v, scale, causal)
+    A_ref, _ = oracle.fwd(q, k, np.abs(v), scale, causal)
+    check_forward(to_np(O), to_np(LSE), O_ref, LSE_ref, DT[dtype], "fwd_ws rising", A_ref, Nk,
+                  float(np.abs(v).max()), max_abs_bar="auto")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_wide_logits(dtype):
+    """Q, K ~ N(0, 4^2) at d = 128: scores spread over hundreds of log2 units,
+    so the vote fires on irregular tiles and row blocks."""
+    inp = synth.make_inputs(1, 2, 260, 900, 128, dtype, 91, sigma_qk=4.0, device="cuda", with_dO=False)
+    scale = 1.0 / math.sqrt(128)
+    say("fwd_ws wide logits", dtype)
+    O, LSE = _ws_fwd(inp, scale, False)
+    O2, L2 = fa.forward(inp["Q"], inp["K"], inp["V"], scale, False)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2) and torch.equal(LSE, L2)
+    q, k, v = oracle_view(inp["Q"]), oracle_view(inp["K"]), oracle_view(inp["V"])
+    O_ref, LSE_ref = oracle.fwd(q, k, v, scale, False)
+    A_ref, _ = oracle.fwd(q, k, np.abs(v), scale, False)
+    check_forward(to_np(O), to_np(LSE), O_ref, LSE_ref, DT[dtype], "fwd_ws wide", A_ref, 900,
+                  float(np.abs(v).max()), max_abs_bar=False)
