@@ -206,3 +206,17 @@ def test_deterministic():
     for _ in range(3):
         O2, L2 = _run_fwd(inp, 0.1, False)
         assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
+def test_o_rel_l2_headroom():
+    """The O rel-L2 bar (1e-3 against the oracle rounded to bf16) at the
+    training shape, with its headroom tracked.  P feeds the P V product as
+    fp16, 2^-12 relative rounding per element; the rows' O is a random-walk
+    average of V (|O| ~ |V| / sqrt(effective keys)), so that rounding moves
+    O by about 2^-12 of itself, some 6 % of a bf16 output ulp, and about that
+    share of outputs lands on the neighbouring bf16 value: rel-L2 8.5e-4 on
+    this config.  A change that adds error anywhere in the forward shows up
+    here before it reaches the bar."""
+    w = synth.WORKLOADS["train_b8h32n4096d128"]
+    e = _sampled_check(w, rows_per_head=32, heads=list(range(0, w.B * w.H, 2)), label="headroom")
+    assert e["O_rel_l2_vs_rounded"] <= 9.5e-4, e
