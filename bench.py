@@ -44,6 +44,8 @@ def parse():
                     help="also run one plain device copy of this many MiB (a known-size reference "
                          "for hardware byte counters)")
     ap.add_argument("--no-sclk", action="store_true", help="skip sampling the graphics clock under load")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip timing the vendor bf16 GEMM (torch.matmul) used as this box's attainable-rate reference")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time the forward alone (implied for workloads that have no backward)")
     ap.add_argument("--dropout", type=float, default=0.0,
@@ -172,6 +174,7 @@ def main():
     step_events = [e[0].elapsed_time(e[-1]) for e in evs]  # fa_fwd start .. last backward stage end
 
     sclk = None if args.no_sclk else sample_sclk(launch_step)
+    gemm_ref = None if args.no_gemm_reference else vendor_gemm_reference()
 
     F = w.fwd_flops()
     total_flops = (1.0 if fwd_only else 3.5) * F
@@ -248,6 +251,7 @@ def main():
         "kernel_ms_spread": {n: spread(v) for n, v in per.items()},
         "peak_mem_bytes": peak_mem,
         "sclk_mhz_under_load": sclk,
+        "vendor_gemm_bf16": gemm_ref,
         "versions": versions(torch),
         "describe": fa.fa_describe(w.d, fa.dtype_code(w.torch_dtype), w.causal),
         "device": torch.cuda.get_device_properties(0).gcnArchName,
@@ -301,6 +305,36 @@ def sample_sclk(launch_step, seconds=4.0):
         return None
     return {"mean": sum(vals) / len(vals), "min": min(vals), "max": max(vals), "xcds": len(vals),
             "source": "amd-smi metric --clock"}
+
+
+def vendor_gemm_reference(m=8192, n=8192, k=8192, iters=40):
+    """A calibration beside the step, not part of it: the sustained rate of the
+    vendor's bf16 GEMM (torch.matmul, i.e. hipBLASLt) on this machine, on N(0, 1)
+    operands and on an all-zero A.  Under sustained load the graphics clock
+    settles where the board's power allows, and that depends on the data the
+    matrix cores switch on, so this is the dense-MFMA rate the box actually
+    delivers, beside the published peak the roofline uses."""
+    import torch
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    a = torch.randn((m, k), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    b = torch.randn((k, n), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    out = {"shape_mnk": [m, n, k], "iters": iters}
+    for name, A in (("tflops", a), ("tflops_zero_a", torch.zeros_like(a))):
+        for _ in range(5):
+            c = A @ b
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            c = A @ b
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = 2.0 * m * n * k / (e0.elapsed_time(e1) / iters * 1e-3) / 1e12
+    del a, b, c
+    out["frac_of_peak"] = out["tflops"] / PEAK_BF16_TFLOPS
+    return out
 
 
 def versions(torch):
