@@ -271,8 +271,9 @@ def spread(v):
 
 
 def sample_sclk(launch_step, seconds=4.0):
-    """Graphics clock (MHz, mean over the XCDs) read with amd-smi while the
-    step runs back to back; None when the tool is missing or says nothing."""
+    """Graphics clock (MHz, mean over the XCDs) and socket power (W) read with
+    amd-smi while the step runs back to back; None when the tool is missing or
+    says nothing."""
     import re
     import subprocess
     import threading
@@ -284,8 +285,8 @@ def sample_sclk(launch_step, seconds=4.0):
     def query():
         time.sleep(seconds / 3)
         try:
-            r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True,
-                               timeout=seconds)
+            r = subprocess.run(["amd-smi", "metric", "--clock", "--power", "--json"], capture_output=True,
+                               text=True, timeout=seconds)
             out["text"] = r.stdout
         except Exception as e:  # tool absent or hung: no reading
             out["error"] = repr(e)
@@ -303,8 +304,10 @@ def sample_sclk(launch_step, seconds=4.0):
     vals = [float(m) for m in re.findall(r'"gfx_\d+":\s*\{\s*"clk":\s*\{\s*"value":\s*([0-9.]+)', text)]
     if not vals:
         return None
+    # "socket_power": {"value": W, "unit": "W"}: the board's draw, against its power cap
+    pw = re.findall(r'"socket_power":\s*\{\s*"value":\s*([0-9.]+)', text)
     return {"mean": sum(vals) / len(vals), "min": min(vals), "max": max(vals), "xcds": len(vals),
-            "source": "amd-smi metric --clock"}
+            "socket_power_w": float(pw[0]) if pw else None, "source": "amd-smi metric --clock --power"}
 
 
 def vendor_gemm_reference(m=8192, n=8192, k=8192, iters=40):
