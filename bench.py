@@ -195,12 +195,14 @@ def main():
         "fa_bwd_dropout (3 kernels)": ("mfma", 2.5 * F),  # the whole backward, 2.5 F by the metric's convention
     }
     dom = max(names, key=lambda n: kern_ms[n])
+    launched = launched_kernels(w, use_ws, drop, splits)
     bound, units = work[dom]
     traffic = measured_traffic(w.name, dom) if splits is None and not drop else None
     if bound == "mfma":
         achieved = units / (kern_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma",
                 "kernel": dom if splits is None else "fwd_kernel (split ranges) + fwd_merge_kernel",
+                "launched": launched.get(dom),
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "flops_per_launch": units, "avg_launch_ms": kern_ms[dom]}
@@ -247,6 +249,7 @@ def main():
         "bwd_tflops": bwd_tflops,
         "fwd_bwd_pct_peak": None if fwd_only else 100.0 * value / PEAK_BF16_TFLOPS,
         "kernel_ms": kern_ms,
+        "kernels_launched": launched,
         "step_ms_events": spread(step_events),
         "kernel_ms_spread": {n: spread(v) for n, v in per.items()},
         "peak_mem_bytes": peak_mem,
@@ -308,6 +311,28 @@ def sample_sclk(launch_step, seconds=4.0):
     pw = re.findall(r'"socket_power":\s*\{\s*"value":\s*([0-9.]+)', text)
     return {"mean": sum(vals) / len(vals), "min": min(vals), "max": max(vals), "xcds": len(vals),
             "socket_power_w": float(pw[0]) if pw else None, "source": "amd-smi metric --clock --power"}
+
+
+def launched_kernels(w, use_ws, drop, splits):
+    """The kernel each timed stage launches for this workload, as the library
+    routes it (d = 128 on 16-bit data without dropout takes the
+    one-wave-per-SIMD kernels; fa_fwd_ws packs V first)."""
+    kv = w.d == 128 and w.dtype in ("bf16", "f16") and not drop
+    if splits is not None:
+        fwd = "fwd_kernel (split ranges) + fwd_merge_kernel"
+    elif use_ws:
+        fwd = "v_pack_kernel + " + ("fwd_r64_kernel" if kv else "fwd_kernel")
+    else:
+        fwd = "fwd_kernel"
+    fwd_name = "v_pack_kernel + fwd_kernel" if use_ws else "fwd_kernel"
+    out = {fwd_name: fwd}
+    if drop:
+        out["fa_bwd_dropout (3 kernels)"] = "bwd_pre_kernel + bwd_dkdv_kernel + bwd_dq_kernel"
+    else:
+        out.update({"bwd_pre_kernel": "bwd_pre_kernel",
+                    "bwd_dkdv_kernel": "bwd_dkdv_kv_kernel" if kv else "bwd_dkdv_kernel",
+                    "bwd_dq_kernel": "bwd_dq_kv_kernel" if kv else "bwd_dq_kernel"})
+    return out
 
 
 def vendor_gemm_reference(m=8192, n=8192, k=8192, iters=40):
