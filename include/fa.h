@@ -95,9 +95,11 @@ fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LS
  *    on entry do not matter, on return unspecified.
  *  - When it pays: the packing pass reads and writes V once, and it saves
  *    each workgroup (256 query rows) its own conversion of every V tile, so
- *    the gain grows with the query tiles per head.  Measured on MI355X:
- *    65536 causal rows +9 %, 4096 rows +3-4 % (d = 128, bf16); 1024 rows
- *    against 8192 keys (d = 64, fp16) 7 % slower than fa_fwd.
+ *    the gain grows with the query tiles per head.  At d = 128 on bf16/fp16
+ *    data the key loop is also a different kernel (four waves of 64 query
+ *    rows, one per SIMD), with the same results.  Measured on MI355X:
+ *    4096 rows +7-9 %, 65536 causal rows +12-14 % (d = 128, bf16); 1024
+ *    rows against 8192 keys (d = 64, fp16) 7 % slower than fa_fwd.
  *  - Everything else as fa_fwd; FA_ERR_INVALID_ARG also for a null,
  *    misaligned or too small workspace.
  */
