@@ -195,7 +195,7 @@ def main():
         "fa_bwd_dropout (3 kernels)": ("mfma", 2.5 * F),  # the whole backward, 2.5 F by the metric's convention
     }
     dom = max(names, key=lambda n: kern_ms[n])
-    launched = launched_kernels(w, use_ws, drop, splits)
+    launched = {n: k for n, k in launched_kernels(w, use_ws, drop, splits).items() if n in names}
     bound, units = work[dom]
     traffic = measured_traffic(w.name, dom) if splits is None and not drop else None
     if bound == "mfma":
