@@ -116,6 +116,26 @@ __device__ __forceinline__ void wait_agpr_loads(u32x4_t (&f)[2][8]) {
                  : "memory");
 }
 
+// Sixteen 16-byte LDS reads straight into AGPRs: f[r][k] from byte address
+// a[k] + 8192 r.  The wait for them sits in the same block, so the tuples hold
+// their values when it returns and no VALU copy stands between them and the
+// products that read them.
+__device__ __forceinline__ void lds_read_agpr(u32x4_t (&f)[2][8], const uint32_t (&a)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %16\n\tds_read_b128 %1, %17\n\tds_read_b128 %2, %18\n\tds_read_b128 %3, %19\n\t"
+        "ds_read_b128 %4, %20\n\tds_read_b128 %5, %21\n\tds_read_b128 %6, %22\n\tds_read_b128 %7, %23\n\t"
+        "ds_read_b128 %8, %16 offset:8192\n\tds_read_b128 %9, %17 offset:8192\n\t"
+        "ds_read_b128 %10, %18 offset:8192\n\tds_read_b128 %11, %19 offset:8192\n\t"
+        "ds_read_b128 %12, %20 offset:8192\n\tds_read_b128 %13, %21 offset:8192\n\t"
+        "ds_read_b128 %14, %22 offset:8192\n\tds_read_b128 %15, %23 offset:8192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=a"(f[0][0]), "=a"(f[0][1]), "=a"(f[0][2]), "=a"(f[0][3]), "=a"(f[0][4]), "=a"(f[0][5]), "=a"(f[0][6]),
+          "=a"(f[0][7]), "=a"(f[1][0]), "=a"(f[1][1]), "=a"(f[1][2]), "=a"(f[1][3]), "=a"(f[1][4]), "=a"(f[1][5]),
+          "=a"(f[1][6]), "=a"(f[1][7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
+
 // A fragment moved to AGPRs once, where mfma_bagpr reads it (the compiler
 // would otherwise keep it in VGPRs and copy it over before every product).
 __device__ __forceinline__ u32x4_t to_agpr(u32x4_t v) {

@@ -39,6 +39,7 @@
 // and the epilogue multiplies by 1 / (1 - rate) together with 1 / l.  The
 // four lanes of a quad (four consecutive query rows) share the generator calls
 // of each 32-key block (fa_common.hpp, dropout_keep_query_lane).
+#include <algorithm>
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -521,51 +522,17 @@ void fwd_r64_kernel(const void *__restrict__ Q, const void *__restrict__ K, void
     constexpr int NKS = D / 16, NDB = D / 32, NKG = BC / 16;
     constexpr int TILE = BC * D * 2;       // bytes of a K tile or of a V^T tile
     constexpr int VS = 2 * TILE;           // K stage s at s TILE, V^T stage s at VS + s TILE
+    constexpr int QS = 4 * TILE;           // the Q tile (BR rows, tile_off<D> layout): 4 TILE bytes
     constexpr int NCP = TILE / 1024 / NW;  // 1 KiB copies per wave per tile and tensor
     constexpr int LEAD = 3, NSLOT = LEAD + 1;
     static_assert(E != ELT_F32, "16-bit K is copied global -> LDS as it is");
-    __shared__ __attribute__((aligned(16))) unsigned char lds[4 * TILE];
+    static_assert(BR * D * 2 == 4 * TILE, "the Q tile fills four tile-sized stages");
+    __shared__ __attribute__((aligned(16))) unsigned char lds[8 * TILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g = lane >> 5;
 
-    int bh, qt;
-    if constexpr (CAUSAL) {
-        const int L = blockIdx.x;  // longest rows first
-        qt = n_qt - 1 - L / BH;
-        bh = L % BH;
-    } else {
-        const int L = xcd_remap(blockIdx.x, gridDim.x);
-        bh = L / n_qt;
-        qt = L % n_qt;
-    }
-    const int64_t q_head = (int64_t)bh * Nq * D;
-    const int64_t k_head = (int64_t)bh * Nk * D;
-    const int q_w0 = qt * BR + 64 * wave;  // first row of this wave
-    const int k_end = CAUSAL ? min(Nk, min(qt * BR + BR, Nq)) : Nk;
-    const int n_kt = (k_end + BC - 1) / BC;
-    const int n_kt_all = (Nk + BC - 1) / BC;  // tiles per head in the packed V^T
-
-    // Q^T fragments (B operands of S^T = K Q^T, k = head dim 16 ks + 8 g + v)
-    // of both row blocks, moved to AGPRs once
-    u32x4_t qf[2][NKS];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int q = q_w0 + 32 * r + l32;
-        const int q_ld = q < Nq ? q : Nq - 1;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qf[r][ks] = load8_operand<E>(Q, q_head + (int64_t)q_ld * D + 16 * ks + 8 * g);
-    }
-    // last key each lane's rows see (past Nk, or causal past the row), less
-    // the lane's 4g offset in the score registers' key order
-    int klim[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) klim[r] = (CAUSAL ? min(q_w0 + 32 * r + l32, Nk - 1) : Nk - 1) - 4 * g;
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qf[r][ks] = to_agpr(qf[r][ks]);
 
     // LDS byte offsets in a stage: a_off[ks] the K fragment (key row l32 of a
     // 32-key block, head dims 16 ks + 8 g .. +7; key block 1 adds 8 KiB);
@@ -582,270 +549,369 @@ void fwd_r64_kernel(const void *__restrict__ Q, const void *__restrict__ K, void
             v_off[p][kg] = (uint32_t)VS + 2u * (uint32_t)(vt_row<BC>(col) * BC + (((2 * kg + g) ^ vt_xor<BC>(col)) * 8));
         }
 
-    // Copies of tile kt into stage s: K rows in blocks of four (1 KiB, the
-    // swizzle applied on the global side; rows past Nk re-read row Nk - 1,
-    // whose scores are masked), V^T tiles as they are.  Block b = wave + 4 jb.
-    const uint16_t *Kh = static_cast<const uint16_t *>(K) + k_head;
-    const unsigned char *Vh = reinterpret_cast<const unsigned char *>(Vpk) + (int64_t)bh * n_kt_all * TILE;
+    // Copies global -> LDS in 1 KiB blocks, block b = wave + 4 jb: K rows 4b ..
+    // 4b + 3 of a tile with the swizzle applied on the global side (rows past
+    // Nk re-read row Nk - 1, whose scores are masked), V^T tiles as they are,
+    // Q rows the same way as K (rows past Nq re-read row Nq - 1, never stored).
+    const int n_kt_all = (Nk + BC - 1) / BC;  // tiles per head in the packed V^T
     const int cp_row = wave * 4 + lane / 16;
     const uint32_t cp_col = (uint32_t)((lane & 15) ^ swz<D>(cp_row)) * 16u;
-    auto copy_tile = [&](int kt, int s, int jb) __attribute__((always_inline)) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 in the clobber list: see the kernel's notes
+    auto copy_tile = [&](int kt, int s, int jb, const uint16_t *Kb, const unsigned char *Vb)
+        __attribute__((always_inline)) {
         const int grow = min(kt * BC + cp_row + 16 * jb, Nk - 1);
         const uint32_t koff = (uint32_t)grow * (uint32_t)(D * 2) + cp_col;
         const uint32_t voff = (uint32_t)kt * (uint32_t)TILE + (uint32_t)((wave + NW * jb) * 1024 + lane * 16);
         const uint32_t dk = (uint32_t)(s * TILE + (wave + NW * jb) * 1024);
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // M0 in the clobber list: see the kernel's notes
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(koff), "s"(Kh), "s"(dk)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(koff), "s"(Kb), "s"(dk)
                      : "memory", "m0");
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(Vh),
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(Vb),
                      "s"(dk + (uint32_t)VS)
                      : "memory", "m0");
+    };
+    auto copy_q = [&](int q0, const uint16_t *Qb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jb = 0; jb < BR / 16; ++jb) {
+            const int grow = min(q0 + cp_row + 16 * jb, Nq - 1);
+            const uint32_t qoff = (uint32_t)grow * (uint32_t)(D * 2) + cp_col;
+            const uint32_t dq = (uint32_t)(QS + (wave + NW * jb) * 1024);
+            asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(qoff), "s"(Qb), "s"(dq)
+                         : "memory", "m0");
+        }
+    };
 #pragma clang diagnostic pop
-    };
 
-    f32x16_t o[2][NDB];
+    // Work items are query tiles.  Causal: one per workgroup, the longest rows
+    // first.  Otherwise the workgroups are persistent: workgroup w takes the
+    // tiles it * gridDim.x + xcd_remap(w), so that in every round an XCD's
+    // workgroups hold consecutive tiles (the same heads' K and V in its L2),
+    // and each item's Q tile and first K/V tile are copied while the item
+    // before it still computes.
+    const int n_items = BH * n_qt;
+    auto item_of = [&](int it) -> int {
+        if constexpr (CAUSAL) return it == 0 ? (int)blockIdx.x : -1;
+        const int L = it * (int)gridDim.x + xcd_remap(blockIdx.x, gridDim.x);
+        return L < n_items ? L : -1;
+    };
+    auto decode = [&](int L, int &bh, int &qt) __attribute__((always_inline)) {
+        if constexpr (CAUSAL) {
+            qt = n_qt - 1 - L / BH;
+            bh = L % BH;
+        } else {
+            bh = L / n_qt;
+            qt = L % n_qt;
+        }
+    };
+    auto k_base = [&](int bh) { return static_cast<const uint16_t *>(K) + (int64_t)bh * Nk * D; };
+    auto v_base = [&](int bh) {
+        return reinterpret_cast<const unsigned char *>(Vpk) + (int64_t)bh * n_kt_all * TILE;
+    };
+    auto q_base = [&](int bh) { return static_cast<const uint16_t *>(Q) + (int64_t)bh * Nq * D; };
+
+    int L = item_of(0);
+    int base = 0;  // the LDS stage of the current item's first tile
+    if (L >= 0) {  // the first item's Q tile and first K / V tile
+        int bh0, qt0;
+        decode(L, bh0, qt0);
+        copy_q(qt0 * BR, q_base(bh0));
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[r][db] = f32x16_t{};
-    float m_used[2] = {kMaxInit, kMaxInit}, l_run[2] = {0.f, 0.f};
-    const f16x2_t ones = {(_Float16)1.f, (_Float16)1.f};
-    // Scores of the current tile [key block][row block]; P as fp16 pairs, the
-    // B operand of each 16-key group [row block][group]; V^T fragments of the
-    // held-over groups 2 and 3 [group - 2][db].  Before the first tile the
-    // held-over part is empty: scores -inf (P = 0) and V^T = 0.
-    f32x16_t sc[2][2];
-    u32x4_t pk[2][NKG], vt[2][NDB];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sc[1][r][e] = -INFINITY;
-        pk[r][2] = u32x4_t{0u, 0u, 0u, 0u};
+        for (int jb = 0; jb < NCP; ++jb) copy_tile(0, 0, jb, k_base(bh0), v_base(bh0));
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) vt[h][db] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int it = 0; L >= 0; ++it) {
+        const int Ln = item_of(it + 1);
+        int bh, qt, bhn = 0, qtn = 0;
+        decode(L, bh, qt);
+        if (Ln >= 0) decode(Ln, bhn, qtn);
+        const int64_t q_head = (int64_t)bh * Nq * D;
+        const int q_w0 = qt * BR + 64 * wave;  // first row of this wave
+        const int k_end = CAUSAL ? min(Nk, min(qt * BR + BR, Nq)) : Nk;
+        const int n_kt = (k_end + BC - 1) / BC;
+        const uint16_t *Kh = k_base(bh);
+        const unsigned char *Vh = v_base(bh);
+        // the next item's first tile goes where this item's tile n_kt would
+        const uint16_t *Kx = Ln >= 0 ? k_base(bhn) : Kh;
+        const unsigned char *Vx = Ln >= 0 ? v_base(bhn) : Vh;
 
-    if (n_kt > 0) {
+        // this item's Q tile and first tile are in LDS once every wave's copies
+        // are (for later items the previous item's step ends already waited
+        // for them: its first step for the Q tile, its last for the K/V tile)
+        if (it == 0) {
+            wait_vmem();
+            __syncthreads();
+        }
+        // Q^T fragments (B operands of S^T = K Q^T, k = head dim 16 ks + 8 g + v)
+        // of both row blocks, from the Q tile into AGPRs.  The swizzle depends
+        // on the row's low four bits only, so the wave's fragment ks of row
+        // block r sits at the K fragment's offset a_off[ks] plus 256 bytes per
+        // row of 64 wave + 32 r.  The wave's part is made opaque per item so
+        // the eight sums are formed here, not kept live over the item loop.
+        uint32_t qb = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char *)lds) +
+                      (uint32_t)(QS + 64 * 256 * wave);
+        asm volatile("" : "+s"(qb));
+        uint32_t qa[NKS];
 #pragma unroll
-        for (int jb = 0; jb < NCP; ++jb) copy_tile(0, 0, jb);
-    }
-    wait_vmem();
-    __syncthreads();
-    mfma_wait<3>();  // the zeroed accumulators, before mfma_acc reads them
+        for (int ks = 0; ks < NKS; ++ks) qa[ks] = qb + a_off[ks];
+        u32x4_t qf[2][NKS];
+        lds_read_agpr(qf, qa);
+        // last key each lane's rows see (past Nk, or causal past the row), less
+        // the lane's 4g offset in the score registers' key order
+        int klim[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) klim[r] = (CAUSAL ? min(q_w0 + 32 * r + l32, Nk - 1) : Nk - 1) - 4 * g;
+        // every wave holds its Q: the tile's space takes the next item's
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (Ln >= 0) copy_q(qtn * BR, q_base(bhn));
 
-    // The exponentials run as a stream of 32 pairs per step, one pair per two
-    // products.  Pair P: P < 8 the previous tile's group 3 (row block P / 4),
-    // then groups 0, 1, 2 of this tile (row block (P % 8) / 4); t = P % 4 picks
-    // register elements 8 (group % 2) + 2t, + 1 of key block group / 2.  Each
-    // element's exponential is issued in a slot of its own (pa) and the pair is
-    // packed to fp16 and added to the row sum a slot later (pb), so the wave
-    // never waits on the transcendental unit's latency.
-    auto pair_of = [](int P, int &kg, int &r, int &t) constexpr {
-        kg = P < 8 ? 3 : (P - 8) / 8;
-        r = (P % 8) / 4;
-        t = P % 4;
-    };
-    float xp[2][2];  // the two exponentials of pairs in flight, by P % 2
-    xp[1][0] = xp[1][1] = 0.f;  // "pair 31 of the tile before the first": P = 0
-    auto pa = [&](int P, int h) __attribute__((always_inline)) {
-        int kg, r, t;
-        pair_of(P, kg, r, t);
-        const int e = 8 * (kg % 2) + 2 * t + h;
-        xp[P % 2][h] = __builtin_amdgcn_exp2f(fmaf(sc[kg / 2][r][e], scale_log2, -m_used[r]));
-    };
-    auto pb = [&](int P) __attribute__((always_inline)) {
-        int kg, r, t;
-        pair_of(P, kg, r, t);
-        // (the word is cast, not the vector element: a cast of an element of a
-        // vector lvalue reads element 0)
-        const uint32_t w = pack_f16(xp[P % 2][0], xp[P % 2][1]);
-        pk[r][kg][t] = w;
-        l_run[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), ones, l_run[r], false);
-    };
+        f32x16_t o[2][NDB];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[r][db] = f32x16_t{};
+        float m_used[2] = {kMaxInit, kMaxInit}, l_run[2] = {0.f, 0.f};
+        const f16x2_t ones = {(_Float16)1.f, (_Float16)1.f};
+        // Scores of the current tile [key block][row block]; P as fp16 pairs, the
+        // B operand of each 16-key group [row block][group]; V^T fragments of the
+        // held-over groups 2 and 3 [group - 2][db].  Before the first tile the
+        // held-over part is empty: scores -inf (P = 0) and V^T = 0.
+        f32x16_t sc[2][2];
+        u32x4_t pk[2][NKG], vt[2][NDB];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sc[1][r][e] = -INFINITY;
+            pk[r][2] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) vt[h][db] = u32x4_t{0u, 0u, 0u, 0u};
+        mfma_wait<3>();  // the zeroed accumulators, before mfma_acc reads them
 
-    // One step over tile kt in stage s, copying tile kn into stage s ^ 1.
-    auto step = [&](int kt, int s, int kn, auto mask_c) __attribute__((always_inline)) {
-        constexpr bool MASK = decltype(mask_c)::value;
-        const uint32_t sb = (uint32_t)(s * TILE);
-        uint32_t ao[NKS], vo[2][NKG];
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) ao[ks] = a_off[ks] + sb;
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-            for (int kg = 0; kg < NKG; ++kg) vo[p][kg] = v_off[p][kg] + sb;
-        const int k0 = kt * BC;
-        u32x4_t opr[NSLOT];
-        float mx[2] = {-INFINITY, -INFINITY}, mt[2], l_prev[2];
-        uint64_t vote[2];
-        // operand of product pair u (products 2u, 2u + 1, one per row block):
-        // u < 16 K fragment (key block u / 8, k-step u % 8); 16..23 held-over
-        // V^T in registers; 24..31 V^T fragment (group (u - 24) / 4, db (u - 24) % 4)
-        auto rd = [&](int u) __attribute__((always_inline)) {
-            if (u < 16) opr[u % NSLOT] = *reinterpret_cast<const u32x4_t *>(lds + ao[u % 8] + (u / 8) * 32 * 256);
-            else if (u >= 24) {
-                const int kg = (u - 24) / 4, db = (u - 24) % 4;
-                opr[u % NSLOT] = *reinterpret_cast<const u32x4_t *>(lds + vo[db % 2][kg] + (db / 2) * 8192);
-            }
+        // The exponentials run as a stream of 32 pairs per step, one pair per two
+        // products.  Pair P: P < 8 the previous tile's group 3 (row block P / 4),
+        // then groups 0, 1, 2 of this tile (row block (P % 8) / 4); t = P % 4 picks
+        // register elements 8 (group % 2) + 2t, + 1 of key block group / 2.  Each
+        // element's exponential is issued in a slot of its own (pa) and the pair is
+        // packed to fp16 and added to the row sum a slot later (pb), so the wave
+        // never waits on the transcendental unit's latency.
+        auto pair_of = [](int P, int &kg, int &r, int &t) constexpr {
+            kg = P < 8 ? 3 : (P - 8) / 8;
+            r = (P % 8) / 4;
+            t = P % 4;
         };
-        auto mm = [&](int i) __attribute__((always_inline)) {
-            const int u = i / 2, r = i % 2;
-            if (u < 16) {
-                const int kb = u / 8, ks = u % 8;
-                if (ks == 0) sc[kb][r] = mfma_bagpr_first<E>(opr[u % NSLOT], qf[r][0]);
-                else mfma_bagpr<E>(sc[kb][r], opr[u % NSLOT], qf[r][ks]);
-            } else if (u < 24) {
-                const int kg = 2 + (u - 16) / 4, db = (u - 16) % 4;
-                mfma_acc<ELT_F16>(o[r][db], vt[kg - 2][db], pk[r][kg]);
-            } else {
-                const int kg = (u - 24) / 4, db = (u - 24) % 4;
-                mfma_acc<ELT_F16>(o[r][db], opr[u % NSLOT], pk[r][kg]);
-            }
+        float xp[2][2];  // the two exponentials of pairs in flight, by P % 2
+        xp[1][0] = xp[1][1] = 0.f;  // "pair 31 of the tile before the first": P = 0
+        auto pa = [&](int P, int h) __attribute__((always_inline)) {
+            int kg, r, t;
+            pair_of(P, kg, r, t);
+            const int e = 8 * (kg % 2) + 2 * t + h;
+            xp[P % 2][h] = __builtin_amdgcn_exp2f(fmaf(sc[kg / 2][r][e], scale_log2, -m_used[r]));
         };
-        // in-lane maximum over elements 4c .. 4c + 3 of key block kb, row block r
-        auto maxq = [&](int kb, int r, int c) __attribute__((always_inline)) {
-            mx[r] = max3(max3(mx[r], sc[kb][r][4 * c], sc[kb][r][4 * c + 1]), sc[kb][r][4 * c + 2], sc[kb][r][4 * c + 3]);
-        };
-        auto do_vote = [&]() __attribute__((always_inline)) {
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                mt[r] = half_max(mx[r]) * scale_log2;  // scale > 0: max commutes with it
-                vote[r] = __ballot(mt[r] > m_used[r] + kRescaleThreshold);
-            }
-        };
-        // masked tiles: the scores of every key past Nk or after the row -> -inf
-        auto mask_block = [&](int kb) __attribute__((always_inline)) {
-#pragma unroll
-            for (int r = 0; r < 2; ++r)
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    if (k0 + 32 * kb + 8 * (e / 4) + (e % 4) > klim[r]) sc[kb][r][e] = -INFINITY;
+        auto pb = [&](int P) __attribute__((always_inline)) {
+            int kg, r, t;
+            pair_of(P, kg, r, t);
+            // (the word is cast, not the vector element: a cast of an element of a
+            // vector lvalue reads element 0)
+            const uint32_t w = pack_f16(xp[P % 2][0], xp[P % 2][1]);
+            pk[r][kg][t] = w;
+            l_run[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), ones, l_run[r], false);
         };
 
-        static_for<LEAD>([&](auto c) __attribute__((always_inline)) { rd(decltype(c)::value); });
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<64>([&](auto nc) __attribute__((always_inline)) {
-            constexpr int n = decltype(nc)::value;
-            if constexpr (MASK && (n == 16 || n == 32)) {
-                // mask a key block once its S^T products are done, and take its maxima
-                mfma_drain();
-                mask_block(n / 16 - 1);
-#pragma unroll
-                for (int c = 0; c < 8; ++c) maxq(n / 16 - 1, c / 4, c % 4);
-                if constexpr (n == 32) do_vote();
+        // One step over tile kt in stage s, copying tile kn of the head at Kn / Vn
+        // (this item's next tile, or the next item's first) into stage s ^ 1.
+        auto step = [&](int kt, int s, int kn, const uint16_t *Kn, const unsigned char *Vn, auto mask_c)
+            __attribute__((always_inline)) {
+            constexpr bool MASK = decltype(mask_c)::value;
+            const uint32_t sb = (uint32_t)(s * TILE);
+            uint32_t ao[NKS], vo[2][NKG];
+    #pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) ao[ks] = a_off[ks] + sb;
+    #pragma unroll
+            for (int p = 0; p < 2; ++p)
+    #pragma unroll
+                for (int kg = 0; kg < NKG; ++kg) vo[p][kg] = v_off[p][kg] + sb;
+            const int k0 = kt * BC;
+            u32x4_t opr[NSLOT];
+            float mx[2] = {-INFINITY, -INFINITY}, mt[2], l_prev[2];
+            uint64_t vote[2];
+            // operand of product pair u (products 2u, 2u + 1, one per row block):
+            // u < 16 K fragment (key block u / 8, k-step u % 8); 16..23 held-over
+            // V^T in registers; 24..31 V^T fragment (group (u - 24) / 4, db (u - 24) % 4)
+            auto rd = [&](int u) __attribute__((always_inline)) {
+                if (u < 16) opr[u % NSLOT] = *reinterpret_cast<const u32x4_t *>(lds + ao[u % 8] + (u / 8) * 32 * 256);
+                else if (u >= 24) {
+                    const int kg = (u - 24) / 4, db = (u - 24) % 4;
+                    opr[u % NSLOT] = *reinterpret_cast<const u32x4_t *>(lds + vo[db % 2][kg] + (db / 2) * 8192);
+                }
+            };
+            auto mm = [&](int i) __attribute__((always_inline)) {
+                const int u = i / 2, r = i % 2;
+                if (u < 16) {
+                    const int kb = u / 8, ks = u % 8;
+                    if (ks == 0) sc[kb][r] = mfma_bagpr_first<E>(opr[u % NSLOT], qf[r][0]);
+                    else mfma_bagpr<E>(sc[kb][r], opr[u % NSLOT], qf[r][ks]);
+                } else if (u < 24) {
+                    const int kg = 2 + (u - 16) / 4, db = (u - 16) % 4;
+                    mfma_acc<ELT_F16>(o[r][db], vt[kg - 2][db], pk[r][kg]);
+                } else {
+                    const int kg = (u - 24) / 4, db = (u - 24) % 4;
+                    mfma_acc<ELT_F16>(o[r][db], opr[u % NSLOT], pk[r][kg]);
+                }
+            };
+            // in-lane maximum over elements 4c .. 4c + 3 of key block kb, row block r
+            auto maxq = [&](int kb, int r, int c) __attribute__((always_inline)) {
+                mx[r] = max3(max3(mx[r], sc[kb][r][4 * c], sc[kb][r][4 * c + 1]), sc[kb][r][4 * c + 2], sc[kb][r][4 * c + 3]);
+            };
+            auto do_vote = [&]() __attribute__((always_inline)) {
+    #pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    mt[r] = half_max(mx[r]) * scale_log2;  // scale > 0: max commutes with it
+                    vote[r] = __ballot(mt[r] > m_used[r] + kRescaleThreshold);
+                }
+            };
+            // masked tiles: the scores of every key past Nk or after the row -> -inf
+            auto mask_block = [&](int kb) __attribute__((always_inline)) {
+    #pragma unroll
+                for (int r = 0; r < 2; ++r)
+    #pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        if (k0 + 32 * kb + 8 * (e / 4) + (e % 4) > klim[r]) sc[kb][r][e] = -INFINITY;
+            };
+
+            static_for<LEAD>([&](auto c) __attribute__((always_inline)) { rd(decltype(c)::value); });
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<64>([&](auto nc) __attribute__((always_inline)) {
+                constexpr int n = decltype(nc)::value;
+                if constexpr (MASK && (n == 16 || n == 32)) {
+                    // mask a key block once its S^T products are done, and take its maxima
+                    mfma_drain();
+                    mask_block(n / 16 - 1);
+    #pragma unroll
+                    for (int c = 0; c < 8; ++c) maxq(n / 16 - 1, c / 4, c % 4);
+                    if constexpr (n == 32) do_vote();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if constexpr (!MASK && n == 16) mfma_wait<7>();  // key block 0's S^T results, before pa reads them
+                if constexpr (n == 48) {
+                    // every product of the previous tile is issued: move the reference
+                    // maximum where the vote says so, rescale O and l, and redo the
+                    // exponentials of groups 0 and 1
+                    if ((vote[0] | vote[1]) != 0) {
+                        keep_branch();
+                        // the accumulators' wait states, with the accumulators as
+                        // operands so that no copy of them is taken before it
+                        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                                     : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]), "+a"(o[1][0]),
+                                       "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3])
+                                     :
+                                     : "memory");
+    #pragma unroll
+                        for (int r = 0; r < 2; ++r) {
+                            // a block that did not vote keeps its maximum: alpha = 1, exact
+                            const float m_new = vote[r] != 0 ? fmaxf(m_used[r], mt[r]) : m_used[r];
+                            const float alpha = __builtin_amdgcn_exp2f(m_used[r] - m_new);
+                            m_used[r] = m_new;
+                            l_run[r] = l_prev[r] * alpha;
+    #pragma unroll
+                            for (int db = 0; db < NDB; ++db) o[r][db] *= alpha;
+                        }
+    #pragma unroll
+                        for (int P = 8; P < 24; ++P) {
+                            pa(P, 0);
+                            pa(P, 1);
+                            pb(P);
+                        }
+                    }
+                    mfma_wait<1>();  // P and the rescaled accumulators, before the products read them
+                }
+                mm(n);
+                if constexpr (n % 2 == 1) {
+                    constexpr int u = n / 2 + LEAD;
+                    if constexpr (u < 32) rd(u);
+                }
+                if constexpr (n >= 1 && n <= NCP) copy_tile(kn, s ^ 1, n - 1, Kn, Vn);
+                // the exponential stream: pair n / 2 - 1 finished (but pair 23's,
+                // which must precede the branch before product 48), pair n / 2 started
+                if constexpr (n % 2 == 0 && n != 48) pb(n == 0 ? 31 : n / 2 - 1);
+                pa(n / 2, n % 2);
+                if constexpr (n == 47) pb(23);
+                if constexpr (n == 17) { l_prev[0] = l_run[0]; l_prev[1] = l_run[1]; }  // before group 0's sums
+                if constexpr (!MASK) {
+                    if constexpr (n == 34) mfma_wait<7>();  // key block 1's S^T results, before the maxima read them
+                    if constexpr (n >= 18 && n < 26) maxq(0, (n - 18) / 4, (n - 18) % 4);
+                    if constexpr (n >= 34 && n < 38) {
+                        maxq(1, (n - 34) / 2, 2 * ((n - 34) % 2));
+                        maxq(1, (n - 34) / 2, 2 * ((n - 34) % 2) + 1);
+                    }
+                    if constexpr (n == 38) do_vote();
+                }
+                // V^T fragments of groups 2, 3 for the next step
+                if constexpr (n >= 48 && n % 2 == 0) {
+                    constexpr int x = (n - 48) / 2, kg = 2 + x / 4, db = x % 4;
+                    vt[kg - 2][db] = *reinterpret_cast<const u32x4_t *>(lds + vo[db % 2][kg] + (db / 2) * 8192);
+                }
                 __builtin_amdgcn_sched_barrier(0);
-            }
-            if constexpr (!MASK && n == 16) mfma_wait<7>();  // key block 0's S^T results, before pa reads them
-            if constexpr (n == 48) {
-                // every product of the previous tile is issued: move the reference
-                // maximum where the vote says so, rescale O and l, and redo the
-                // exponentials of groups 0 and 1
-                if ((vote[0] | vote[1]) != 0) {
-                    keep_branch();
-                    // the accumulators' wait states, with the accumulators as
-                    // operands so that no copy of them is taken before it
-                    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]), "+a"(o[1][0]),
-                                   "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3])
-                                 :
-                                 : "memory");
-#pragma unroll
-                    for (int r = 0; r < 2; ++r) {
-                        // a block that did not vote keeps its maximum: alpha = 1, exact
-                        const float m_new = vote[r] != 0 ? fmaxf(m_used[r], mt[r]) : m_used[r];
-                        const float alpha = __builtin_amdgcn_exp2f(m_used[r] - m_new);
-                        m_used[r] = m_new;
-                        l_run[r] = l_prev[r] * alpha;
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db) o[r][db] *= alpha;
-                    }
-#pragma unroll
-                    for (int P = 8; P < 24; ++P) {
-                        pa(P, 0);
-                        pa(P, 1);
-                        pb(P);
-                    }
-                }
-                mfma_wait<1>();  // P and the rescaled accumulators, before the products read them
-            }
-            mm(n);
-            if constexpr (n % 2 == 1) {
-                constexpr int u = n / 2 + LEAD;
-                if constexpr (u < 32) rd(u);
-            }
-            if constexpr (n >= 1 && n <= NCP) copy_tile(kn, s ^ 1, n - 1);
-            // the exponential stream: pair n / 2 - 1 finished (but pair 23's,
-            // which must precede the branch before product 48), pair n / 2 started
-            if constexpr (n % 2 == 0 && n != 48) pb(n == 0 ? 31 : n / 2 - 1);
-            pa(n / 2, n % 2);
-            if constexpr (n == 47) pb(23);
-            if constexpr (n == 17) { l_prev[0] = l_run[0]; l_prev[1] = l_run[1]; }  // before group 0's sums
-            if constexpr (!MASK) {
-                if constexpr (n == 34) mfma_wait<7>();  // key block 1's S^T results, before the maxima read them
-                if constexpr (n >= 18 && n < 26) maxq(0, (n - 18) / 4, (n - 18) % 4);
-                if constexpr (n >= 34 && n < 38) {
-                    maxq(1, (n - 34) / 2, 2 * ((n - 34) % 2));
-                    maxq(1, (n - 34) / 2, 2 * ((n - 34) % 2) + 1);
-                }
-                if constexpr (n == 38) do_vote();
-            }
-            // V^T fragments of groups 2, 3 for the next step
-            if constexpr (n >= 48 && n % 2 == 0) {
-                constexpr int x = (n - 48) / 2, kg = 2 + x / 4, db = x % 4;
-                vt[kg - 2][db] = *reinterpret_cast<const u32x4_t *>(lds + vo[db % 2][kg] + (db / 2) * 8192);
-            }
+            });
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+
+
+        // Tiles that need no mask first: every key exists and, causal, precedes
+        // the workgroup's first row.  The rest take the masked variant in a loop of
+        // their own.  The last step copies the next item's first tile.
+        int n_full = Nk / BC;
+        if constexpr (CAUSAL) n_full = min(n_full, (qt * BR + 1) / BC);
+        n_full = min(n_full, n_kt);
+        int kt = 0;
+        for (; kt < n_full; ++kt) {
+            const bool last = kt + 1 == n_kt;
+            step(kt, (base + kt) & 1, last ? 0 : kt + 1, last ? Kx : Kh, last ? Vx : Vh, std::false_type{});
+        }
+        for (; kt < n_kt; ++kt) {
+            const bool last = kt + 1 == n_kt;
+            step(kt, (base + kt) & 1, last ? 0 : kt + 1, last ? Kx : Kh, last ? Vx : Vh, std::true_type{});
+        }
+        base = (base + n_kt) & 1;
+
+        // the last tile's group 2 sums and group 3, then its held-over products
+        pb(31);
+        static_for<8>([&](auto c) __attribute__((always_inline)) {
+            constexpr int P = decltype(c)::value;
+            pa(P, 0);
+            pa(P, 1);
+            pb(P);
+        });
+        mfma_wait<1>();
+        static_for<16>([&](auto c) __attribute__((always_inline)) {
+            constexpr int i = decltype(c)::value, kg = 2 + i / 8, db = (i % 8) / 2, r = i % 2;
+            mfma_acc<ELT_F16>(o[r][db], vt[kg - 2][db], pk[r][kg]);
             __builtin_amdgcn_sched_barrier(0);
         });
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-    };
+        mfma_drain();  // mfma_acc results, before they are read
 
-    // Tiles that need no mask first: every key exists and, causal, precedes
-    // the workgroup's first row.  The rest take the masked variant in a loop of
-    // their own.
-    int n_full = Nk / BC;
-    if constexpr (CAUSAL) n_full = min(n_full, (qt * BR + 1) / BC);
-    n_full = min(n_full, n_kt);
-    int kt = 0;
-    for (; kt < n_full; ++kt) step(kt, kt & 1, kt + 1 < n_kt ? kt + 1 : kt, std::false_type{});
-    for (; kt < n_kt; ++kt) step(kt, kt & 1, kt + 1 < n_kt ? kt + 1 : kt, std::true_type{});
-
-    // the last tile's group 2 sums and group 3, then its held-over products
-    pb(31);
-    static_for<8>([&](auto c) __attribute__((always_inline)) {
-        constexpr int P = decltype(c)::value;
-        pa(P, 0);
-        pa(P, 1);
-        pb(P);
-    });
-    mfma_wait<1>();
-    static_for<16>([&](auto c) __attribute__((always_inline)) {
-        constexpr int i = decltype(c)::value, kg = 2 + i / 8, db = (i % 8) / 2, r = i % 2;
-        mfma_acc<ELT_F16>(o[r][db], vt[kg - 2][db], pk[r][kg]);
-        __builtin_amdgcn_sched_barrier(0);
-    });
-    mfma_drain();  // mfma_acc results, before they are read
-
-    // ---- epilogue: O = u / l, LSE = (m_used + log2 l) * ln 2
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const float l_tot = half_sum(l_run[r]);
-        const float inv = 1.f / l_tot;
-        const int q = q_w0 + 32 * r + l32;
-        if (q < Nq) {
-            const int64_t orow = q_head + (int64_t)q * D;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int rq = 0; rq < 4; ++rq)
-                    store4<E>(O, orow + db * 32 + 8 * rq + 4 * g, o[r][db][4 * rq] * inv, o[r][db][4 * rq + 1] * inv,
-                              o[r][db][4 * rq + 2] * inv, o[r][db][4 * rq + 3] * inv);
-            if (g == 0) LSE[(int64_t)bh * Nq + q] = (m_used[r] + __builtin_log2f(l_tot)) * kLn2;
+        // ---- epilogue: O = u / l, LSE = (m_used + log2 l) * ln 2
+    #pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const float l_tot = half_sum(l_run[r]);
+            const float inv = 1.f / l_tot;
+            const int q = q_w0 + 32 * r + l32;
+            if (q < Nq) {
+                const int64_t orow = q_head + (int64_t)q * D;
+    #pragma unroll
+                for (int db = 0; db < NDB; ++db)
+    #pragma unroll
+                    for (int rq = 0; rq < 4; ++rq)
+                        store4<E>(O, orow + db * 32 + 8 * rq + 4 * g, o[r][db][4 * rq] * inv, o[r][db][4 * rq + 1] * inv,
+                                  o[r][db][4 * rq + 2] * inv, o[r][db][4 * rq + 3] * inv);
+                if (g == 0) LSE[(int64_t)bh * Nq + q] = (m_used[r] + __builtin_log2f(l_tot)) * kLn2;
+            }
         }
+
+        L = Ln;
     }
 }
 
@@ -898,6 +964,18 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(SplitOut part, int G, in
     if (c4 == 0) LSE[row] = (m_star + __builtin_log2f(l)) * kLn2;
 }
 
+// Compute units of the current device (cached per device; every MI355X has 256).
+static int compute_units() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        cached[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+    }
+    return cached[dev];
+}
+
 template <int D, int E, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs &a) {
     constexpr int BC = fwd_keys<D>(), NW = FA_FWD_WAVES, BR = 32 * NW;
@@ -919,7 +997,11 @@ static hipError_t launch_fwd_t(const FwdArgs &a) {
         if (e != hipSuccess) return e;
         if constexpr (D == 128 && E != ELT_F32 && BC == 64 && BR == 256 && FA_FWD_R64) {
             // 64 query rows per wave, one wave per SIMD, over the same 256-row tiles
-            hipLaunchKernelGGL((fwd_r64_kernel<E, CAUSAL>), dim3(BH * n_qt), dim3(256), 0, st, a.Q, a.K, a.O, a.LSE,
+            // causal: one query tile per workgroup; otherwise one persistent
+            // workgroup per compute unit walks the tiles
+            const int items = BH * n_qt;
+            const int grid = CAUSAL ? items : std::min(items, compute_units());
+            hipLaunchKernelGGL((fwd_r64_kernel<E, CAUSAL>), dim3(grid), dim3(256), 0, st, a.Q, a.K, a.O, a.LSE,
                                BH, a.Nq, a.Nk, sl2, n_qt, a.Vpk);
             return hipGetLastError();
         }
@@ -973,7 +1055,8 @@ const char *describe_fwd() {
            "double-buffered K/V^T in LDS, S^T=KQ^T bf16/f16 MFMA 32x32x16, PV fp16 MFMA, lazy rescale>; "
            "fa_fwd_ws: v_pack_kernel (V -> fp16 V^T tiles in the LDS layout), then the key loop copies them; "
            "at d=128 on bf16/fp16 the key loop is fwd_r64_kernel<4 waves, one per SIMD, 64 query rows each, "
-           "fixed 64-product program per 64-key tile, the last 32 keys' PV products held over to the next tile>";
+           "fixed 64-product program per 64-key tile, the last 32 keys' PV products held over to the next tile; "
+           "non-causal: one persistent workgroup per CU over the query tiles>";
 }
 
 }  // namespace fa
