@@ -166,3 +166,64 @@ def test_inline_products_keep_their_wait_states(assembly):
         for x in b[:5]:
             print(n[:60], x)
     assert not bad, {n: len(b) for n, b in bad.items()}
+
+
+# Exponentials per matrix product in each one-wave-per-SIMD kernel's step
+# program: the forward issues one per product (64 keys x 64 rows per wave per
+# 64 products), dK/dV one per two (32 per 64), dQ two per three (64 per 96).
+EXP_PER_PRODUCT = {"fwd_r64_kernel": 1.0, "bwd_dkdv_kv_kernel": 0.5, "bwd_dq_kv_kernel": 2.0 / 3.0}
+
+
+def _blocks(lines):
+    """Straight-line blocks of a function: (label, instructions)."""
+    out, cur, lab = [], [], "entry"
+    for ln in lines:
+        t = ln.split(";")[0].strip()
+        if re.match(r"^\.?LBB\w*:", t):
+            out.append((lab, cur))
+            cur, lab = [], t
+            continue
+        if t and not t.startswith("."):
+            cur.append(t)
+    out.append((lab, cur))
+    return out
+
+
+def interleaving_gaps(lines, per_product):
+    """Blocks that hold a step's products (16 or more) but fewer of its
+    exponentials than the step program puts beside them: the compiler moved
+    vector work away from the products that were to hide it."""
+    bad = []
+    for lab, b in _blocks(lines):
+        n_mfma = sum(1 for t in b if t.startswith("v_mfma"))
+        n_exp = sum(1 for t in b if t.startswith("v_exp_f32"))
+        if n_mfma >= 16 and n_exp < per_product * n_mfma:
+            bad.append((lab, n_mfma, n_exp))
+    return bad
+
+
+def test_interleaving_checker_catches_a_moved_exponential():
+    prods = ["v_mfma_f32_32x32x16_bf16 v[0:15], v[2:5], a[0:3], v[0:15]"] * 16
+    assert interleaving_gaps([".LBB0_1:", *prods, *["v_exp_f32_e32 v1, v1"] * 16], 1.0) == []
+    moved = [".LBB0_1:", *prods, *["v_exp_f32_e32 v1, v1"] * 8, ".LBB0_2:", *["v_exp_f32_e32 v1, v1"] * 8]
+    assert interleaving_gaps(moved, 1.0) == [(".LBB0_1:", 16, 8)]
+
+
+def test_step_exponentials_stay_beside_the_products(assembly):
+    """Each step of the one-wave-per-SIMD kernels interleaves its softmax
+    exponentials with its matrix products, and only that hides them.  A
+    change that lets the compiler sink them into a rarely taken branch's
+    join (it did once: the forward's rescale branch) keeps every result and
+    loses the overlap; this fails on it."""
+    seen = set()
+    bad = {}
+    for n, f in assembly.items():
+        m = re.search(r"_ZN2fa\d+(\w+?_kernel)", n)
+        if not m or m.group(1) not in EXP_PER_PRODUCT:
+            continue
+        seen.add(m.group(1))
+        gaps = interleaving_gaps(f, EXP_PER_PRODUCT[m.group(1)])
+        if gaps:
+            bad[n] = gaps
+    assert seen == set(EXP_PER_PRODUCT), seen
+    assert not bad, bad
