@@ -124,6 +124,8 @@ def main():
         dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
         ws = fa.alloc_workspace(Q, K)
         nst = 1 if drop else fa.fa_bwd_num_stages()
+        if not drop and bwd_dq_first(w):
+            nst = 2  # dQ (forming D), dK/dV; the library's stage 2 launches nothing on this path
 
     def launch_step(events=None):
         if events is not None:
@@ -163,8 +165,9 @@ def main():
 
     # the forward slot: fa_fwd_ws launches the V^T packing kernel and then the key loop
     fwd_name = "v_pack_kernel + fwd_kernel" if use_ws else "fwd_kernel"
-    names = [fwd_name] + (["fa_bwd_dropout (3 kernels)"] if drop else
-                              ["bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"][:nst])
+    stage_names = ["bwd_dq_kernel", "bwd_dkdv_kernel"] if bwd_dq_first(w) else \
+        ["bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
+    names = [fwd_name] + (["fa_bwd_dropout (3 kernels)"] if drop else stage_names[:nst])
     per = {n: [] for n in names}
     for e in evs:
         for k, n in enumerate(names):
@@ -313,6 +316,14 @@ def sample_sclk(launch_step, seconds=4.0):
             "socket_power_w": float(pw[0]) if pw else None, "source": "amd-smi metric --clock --power"}
 
 
+def bwd_dq_first(w):
+    """The library's backward order for this workload without dropout: at
+    d = 128 on 16-bit data the dQ pass runs first and forms D = rowsum(dO * O)
+    itself (stage 0), the dK/dV pass follows (stage 1); elsewhere D, dK/dV,
+    dQ (stages 0, 1, 2)."""
+    return w.d == 128 and w.dtype in ("bf16", "f16")
+
+
 def launched_kernels(w, use_ws, drop, splits):
     """The kernel each timed stage launches for this workload, as the library
     routes it (d = 128 on 16-bit data without dropout takes the
@@ -329,9 +340,10 @@ def launched_kernels(w, use_ws, drop, splits):
     if drop:
         out["fa_bwd_dropout (3 kernels)"] = "bwd_pre_kernel + bwd_dkdv_kernel + bwd_dq_kernel"
     else:
-        out.update({"bwd_pre_kernel": "bwd_pre_kernel",
-                    "bwd_dkdv_kernel": "bwd_dkdv_kv_kernel" if kv else "bwd_dkdv_kernel",
-                    "bwd_dq_kernel": "bwd_dq_kv_kernel" if kv else "bwd_dq_kernel"})
+        if not kv:
+            out["bwd_pre_kernel"] = "bwd_pre_kernel"
+        out.update({"bwd_dkdv_kernel": "bwd_dkdv_kv_kernel" if kv else "bwd_dkdv_kernel",
+                    "bwd_dq_kernel": "bwd_dq_kv_kernel (forms D first)" if kv else "bwd_dq_kernel"})
     return out
 
 

@@ -196,11 +196,13 @@ fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, con
  * fa_bwd split into its kernel launches, for callers that schedule or time
  * them one by one.  fa_bwd_num_stages() returns the number of stages;
  * running fa_bwd_stage(0..n-1, ...) in order on one stream, with the same
- * arguments and workspace, is exactly fa_bwd.  Stage 0 computes
+ * arguments and workspace, is exactly fa_bwd.  In general stage 0 computes
  * D = rowsum(dO * O) into the workspace, stage 1 is the K/V-stationary pass
  * that writes dK and dV, stage 2 the Q-stationary pass that writes dQ
- * (stages 1 and 2 both read D).  Same argument checks as fa_bwd; an unknown
- * stage returns FA_ERR_INVALID_ARG.
+ * (stages 1 and 2 both read D).  At d = 128 on bf16/fp16 data stage 0 is
+ * the Q-stationary pass, which writes dQ and forms D itself, stage 1 the
+ * K/V-stationary pass, and stage 2 launches nothing.  Same argument checks
+ * as fa_bwd; an unknown stage returns FA_ERR_INVALID_ARG.
  */
 int fa_bwd_num_stages(void);
 

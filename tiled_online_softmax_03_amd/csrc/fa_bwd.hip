@@ -945,8 +945,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
 template <int E, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, const void *__restrict__ V,
-                      const void *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Dvec,
-                      void *__restrict__ dQ, int BH, int Nq, int Nk, float scale, float scale_log2, int n_qt) {
+                      const void *__restrict__ O, const void *__restrict__ dO, const float *__restrict__ LSE,
+                      float *__restrict__ Dvec, void *__restrict__ dQ, int BH, int Nq, int Nk, float scale,
+                      float scale_log2, int n_qt) {
     constexpr int D = 128, NW = 4, BR = 64 * NW, BC = 64;
     constexpr int NKS = D / 16;       // k-steps over the head dim
     constexpr int NDB = D / 32;       // 32-column blocks of dQ^T
@@ -982,6 +983,10 @@ void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, co
 
     // Q^T and dO^T fragments of both row blocks (B operands, k = head-dim index
     // 16*ks + 8*g + v, lane = row q_w0 + 32 r + l32) and the rows' statistics.
+    // This pass runs first and forms D = rowsum(dO * O) itself ([RA] section
+    // 04's D term): each lane adds its 64 head dims of the row in fp32, the
+    // permlane32 swap adds the two halves (the same sum in both lanes), and
+    // the g = 0 lanes store it for the dK/dV pass that follows.
     u32x4_t qf[2][NKS], df[2][NKS];
     float lse2[2], dv[2];
 #pragma unroll
@@ -994,7 +999,20 @@ void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, co
             df[r][ks] = load8_operand<E>(dO, q_head + (int64_t)q_ld * D + 16 * ks + 8 * g);
         }
         lse2[r] = LSE[(int64_t)bh * Nq + q_ld] * kLog2e;
-        dv[r] = Dvec[(int64_t)bh * Nq + q_ld];
+        float acc = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            float o8[8];
+            load8_float<E>(O, q_head + (int64_t)q_ld * D + 16 * ks + 8 * g, o8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w = df[r][ks][i];
+                acc = fmaf(o8[2 * i], E == ELT_BF16 ? bf16_lo(w) : f16_lo(w), acc);
+                acc = fmaf(o8[2 * i + 1], E == ELT_BF16 ? bf16_hi(w) : f16_hi(w), acc);
+            }
+        }
+        dv[r] = half_sum(acc);
+        if (g == 0 && q < Nq) Dvec[(int64_t)bh * Nq + q] = dv[r];
     }
     // last key each lane's rows see (past Nk, or causal past the row), less
     // the lane's 4g offset in the score registers' key order
@@ -1233,14 +1251,26 @@ static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
     const int BH = a.B * a.H;
     const int64_t rows = (int64_t)BH * a.Nq;
     const float sl2 = a.scale * kLog2e;
-    if (stage < 0 || stage == 0) {
+    const bool drop = a.drop.t > 0;
+    // d = 128 on 16-bit data without dropout: the dQ pass runs first and forms
+    // D itself (stage 0), then the dK/dV pass (stage 1); stage 2 launches nothing
+    const bool dq_first = D == 128 && E != ELT_F32 && FA_DQ_KV && !drop;
+    if (dq_first) {
+        if (stage < 0 || stage == 0) {
+            const int n_qt = (a.Nq + 255) / 256;
+            if constexpr (D == 128 && E != ELT_F32)
+                hipLaunchKernelGGL((bwd_dq_kv_kernel<E, CAUSAL>), dim3(BH * n_qt), dim3(256), 0, st, a.Q, a.K, a.V,
+                                   a.O, a.dO, a.LSE, a.Dvec, a.dQ, BH, a.Nq, a.Nk, a.scale, sl2, n_qt);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    } else if (stage < 0 || stage == 0) {
         constexpr int RPB = 256 / (D / 8);
         hipLaunchKernelGGL((bwd_pre_kernel<D, E>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, a.O,
                            a.dO, a.Dvec, rows);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const bool drop = a.drop.t > 0;
     if (stage < 0 || stage == 1) {
         const int n_kt = (a.Nk + 127) / 128;
         if constexpr (D == 128 && E != ELT_F32 && FA_DKDV_KV) {
@@ -1262,15 +1292,8 @@ static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
         if (e != hipSuccess) return e;
     }
 dq:
-    if (stage < 0 || stage == 2) {
+    if ((stage < 0 || stage == 2) && !dq_first) {
         const int n_qt = (a.Nq + 255) / 256;
-        if constexpr (D == 128 && E != ELT_F32 && FA_DQ_KV) {
-            if (!drop) {
-                hipLaunchKernelGGL((bwd_dq_kv_kernel<E, CAUSAL>), dim3(BH * n_qt), dim3(256), 0, st, a.Q, a.K, a.V, a.dO,
-                                   a.LSE, a.Dvec, a.dQ, BH, a.Nq, a.Nk, a.scale, sl2, n_qt);
-                return hipGetLastError();
-            }
-        }
         constexpr int BC = dq_keys<D, E>();
         if (drop)
             hipLaunchKernelGGL((bwd_dq_kernel<D, BC, E, CAUSAL, true>), dim3(BH * n_qt), dim3(512), 0, st, a.Q, a.K, a.V,
@@ -1304,12 +1327,12 @@ hipError_t launch_bwd(const BwdArgs &a, int stage) {
 
 const char *describe_bwd() {
     return "bwd_pre_kernel (D=rowsum(dO*O)) -> bwd_dkdv_kernel<D, 8 waves = 4 key groups x 2 query halves, "
-           "128 keys, 64-row query steps (128 at d=64), "
-           "double-buffered Q/dO, transposed LDS reads> (d=128 16-bit without dropout: bwd_dkdv_kv_kernel<4 waves, "
-           "one per SIMD, 32 keys each with K/V fragments in registers, dV/dK accumulators in AGPRs, 64-row steps "
-           "as a fixed product/softmax program>) -> bwd_dq_kernel<D, 8 waves x 32 rows, 64-key tiles (128 at d=64)> "
-           "(d=128 16-bit without dropout: bwd_dq_kv_kernel<4 waves, one per SIMD, 64 rows each, Q^T in AGPRs, "
-           "dQ accumulators in AGPRs, 64-key tiles as a fixed program>); no atomics";
+           "128 keys, 64-row query steps (128 at d=64), double-buffered Q/dO, transposed LDS reads> -> "
+           "bwd_dq_kernel<D, 8 waves x 32 rows, 64-key tiles (128 at d=64)>; d=128 16-bit without dropout: "
+           "bwd_dq_kv_kernel<4 waves, one per SIMD, 64 rows each, Q^T and dQ accumulators in AGPRs, 64-key tiles "
+           "as a fixed program, forms D itself> -> bwd_dkdv_kv_kernel<4 waves, one per SIMD, 32 keys each with K/V "
+           "fragments in registers, dV/dK accumulators in AGPRs, 64-row steps as a fixed product/softmax program>; "
+           "no atomics";
 }
 
 }  // namespace fa
