@@ -149,13 +149,22 @@ def test_bwd_deterministic():
         assert torch.equal(dK1, dK2) and torch.equal(dV1, dV2) and torch.equal(dQ1, dQ2)
 
 
-def test_stages_equal_fa_bwd():
-    """fa_bwd_stage(0..n-1) in order is exactly fa_bwd."""
-    inp = synth.make_inputs(1, 3, 333, 200, 64, "f16", 11, device="cuda")
-    O, LSE, dQ, dK, dV = _run(inp, 0.125, True)
+@pytest.mark.parametrize("d,dtype,causal", [(64, "f16", True), (128, "bf16", False), (128, "f16", True)])
+def test_stages_equal_fa_bwd(d, dtype, causal):
+    """fa_bwd_stage(0..n-1) in order is exactly fa_bwd.  At d = 128 on 16-bit
+    data stage 0 is the dQ pass (which forms D) and stage 1 the dK/dV pass, so
+    those two alone already give fa_bwd's bits and stage 2 changes nothing."""
+    inp = synth.make_inputs(1, 3, 333, 200, d, dtype, 11, device="cuda")
+    say("bwd stages", (1, 3, 333, 200, d, dtype, causal))
+    O, LSE, dQ, dK, dV = _run(inp, 0.125, causal)
     ws = fa.alloc_workspace(inp["Q"], inp["K"])
-    sQ, sK, sV = torch.empty_like(dQ), torch.empty_like(dK), torch.empty_like(dV)
+    sQ, sK, sV = (torch.full_like(t, float("nan")) for t in (dQ, dK, dV))
     for st in range(fa.fa_bwd_num_stages()):
-        fa.fa_bwd_stage(st, inp["Q"], inp["K"], inp["V"], O, inp["dO"], LSE, sQ, sK, sV, ws, 0.125, True)
-    torch.cuda.synchronize()
+        fa.fa_bwd_stage(st, inp["Q"], inp["K"], inp["V"], O, inp["dO"], LSE, sQ, sK, sV, ws, 0.125, causal)
+        torch.cuda.synchronize()
+        if d == 128 and st == 0:
+            assert torch.equal(sQ, dQ), "stage 0 writes dQ on this path"
+            assert torch.isnan(sK).all() and torch.isnan(sV).all()
+        if d == 128 and st == 1:
+            assert torch.equal(sK, dK) and torch.equal(sV, dV), "stage 1 writes dK, dV on this path"
     assert torch.equal(sQ, dQ) and torch.equal(sK, dK) and torch.equal(sV, dV)
