@@ -40,6 +40,7 @@
 // four lanes of a quad (four consecutive query rows) share the generator calls
 // of each 32-key block (fa_common.hpp, dropout_keep_query_lane).
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -964,16 +965,19 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(SplitOut part, int G, in
     if (c4 == 0) LSE[row] = (m_star + __builtin_log2f(l)) * kLn2;
 }
 
-// Compute units of the current device (cached per device; every MI355X has 256).
+// Compute units of the current device (cached per device; every MI355X has
+// 256).  Callers on several host threads may race to fill an entry: they
+// store the same value, through an atomic.
 static int compute_units() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        cached[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 template <int D, int E, bool CAUSAL>
