@@ -38,6 +38,7 @@
 // dP becomes Z (dO V^T) / (1 - rate), and dS = P (dP - D) with the undropped
 // P; D = rowsum(dO * O) still equals sum_j P_ij dP_ij because O is the
 // dropped forward's output.
+#include <algorithm>
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -456,6 +457,10 @@ void bwd_dkdv_kernel(const void *__restrict__ Q, const void *__restrict__ K, con
 //    this order.
 //  * LDS addresses are one per-lane offset per operand shape plus an
 //    immediate (tensor and row block); the stage is added once per step.
+//  * Non-causal launches are persistent: one workgroup per compute unit walks
+//    the key blocks, and each block's K and V rows reach LDS (where the waves
+//    read their fragments) during the last step of the block before it,
+//    together with its first Q/dO tile and that tile's statistics.
 #ifndef FA_KV_ROWS
 #define FA_KV_ROWS 64  // query rows per step (128 measured 2 % slower)
 #endif
@@ -480,42 +485,40 @@ void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, 
     static_assert(E != ELT_F32, "16-bit operands are copied global -> LDS as they are");
     static_assert(BQ == 64 || BQ == 128, "two or four row blocks per step");
     static_assert(BQ * 2 == 64 * NW || BQ == 64 * NW / 4, "one statistics row of 64 per wave or half the waves");
-    // stage s: Q at 2 s TILE, dO at (2 s + 1) TILE
-    __shared__ __attribute__((aligned(16))) unsigned char lds[ST + 2 * 8 * BQ + 512];
+    // stage s: Q at 2 s TILE, dO at (2 s + 1) TILE; statistics; then the K and V
+    // rows of the workgroup's key block (KV, 2 x BKC rows of 256 bytes, tile_off
+    // layout), copied global -> LDS while the item before it computes
+    constexpr int KV = ST + 2 * 8 * BQ + 512, KVB = BKC * D * 2;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[KV + 2 * KVB];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g = lane >> 5;
 
-    int bh, kt;
-    if constexpr (CAUSAL) {
-        const int L = blockIdx.x;  // low key tiles meet the most query rows: first
-        kt = L / BH;
-        bh = L % BH;
-    } else {
-        const int L = xcd_remap(blockIdx.x, gridDim.x);
-        bh = L / n_kt;
-        kt = L % n_kt;
-    }
-    const int64_t q_head = (int64_t)bh * Nq * D;
-    const int64_t k_head = (int64_t)bh * Nk * D;
-    const int k0 = kt * BKC;
-    const int kw0 = k0 + wave * 32;  // first key of this wave
-    const int kw = kw0 + l32;        // this lane's key
-    const int kw_ld = kw < Nk ? kw : Nk - 1;  // keys past Nk compute on a real row and are never stored
-    const int kwg = kw - 4 * g;  // the key less the lane's 4g offset in the score registers' row order
-
+    // Work items are key blocks.  Causal: one per workgroup, the low key tiles
+    // (which meet the most query rows) first.  Otherwise the workgroups are
+    // persistent: workgroup w takes the blocks it * gridDim.x + xcd_remap(w), and
+    // each item's K/V rows and first Q/dO tile are copied while the item before
+    // it computes.
+    const int n_items = BH * n_kt;
+    auto item_of = [&](int it) -> int {
+        if constexpr (CAUSAL) return it == 0 ? (int)blockIdx.x : -1;
+        const int L = it * (int)gridDim.x + xcd_remap(blockIdx.x, gridDim.x);
+        return L < n_items ? L : -1;
+    };
+    auto decode = [&](int L, int &bh_, int &kt_) __attribute__((always_inline)) {
+        if constexpr (CAUSAL) {
+            kt_ = L / BH;
+            bh_ = L % BH;
+        } else {
+            bh_ = L / n_kt;
+            kt_ = L % n_kt;
+        }
+    };
     const int n_qt = (Nq + BQ - 1) / BQ;
-    const int qt_begin = CAUSAL ? min(k0 / BQ, n_qt) : 0;  // earlier rows see none of these keys
-
-    // K and -V fragments: lane = key, k = head-dim index 16*ks + 8*g + v.
-    u32x4_t kf[NKS], vn[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        kf[ks] = load8_operand<E>(K, k_head + (int64_t)kw_ld * D + 16 * ks + 8 * g);
-        const u32x4_t v = load8_operand<E>(V, k_head + (int64_t)kw_ld * D + 16 * ks + 8 * g);
-        vn[ks] = v ^ 0x80008000u;  // sign of both 16-bit halves
-    }
+    // the current item (updated at the top of the item loop)
+    int bh = 0, kt = 0, k0 = 0, kw = 0, kwg = 0, qt_begin = 0;
+    int64_t q_head = 0, k_head = 0;
 
     // Per-lane LDS byte offsets in a tile (tile_off<128> layout):
     //  a_off[ks]: the A operand (row l32, head dims 16ks + 8g .. +7);
@@ -538,35 +541,56 @@ void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, 
     // lane l fetches row 4b + l/16, 16-byte chunk (l % 16) ^ swz(row), which the
     // swizzle places at byte 16 l of the block.  Block b = wave + 4 jb, so the
     // swizzle of a lane's row is the same for every jb.
-    const uint16_t *Qh = static_cast<const uint16_t *>(Q) + q_head;
-    const uint16_t *dOh = static_cast<const uint16_t *>(dO) + q_head;
+    auto q_base = [&](int bh_) { return static_cast<const uint16_t *>(Q) + (int64_t)bh_ * Nq * D; };
+    auto do_base = [&](int bh_) { return static_cast<const uint16_t *>(dO) + (int64_t)bh_ * Nq * D; };
     const int cp_row = wave * 4 + lane / 16;  // + 16 jb
     const uint32_t cp_col = (uint32_t)((lane & 15) ^ swz<D>(cp_row)) * 16u;  // byte offset of the chunk in its row
     // Row statistics of a tile: wave w loads 64 rows of one of them (LSE for
     // w < NW / 2, D for the rest; at BQ = 64 waves 1 and 3 load rows nobody
     // uses), one value per lane.
     const int st_kind = wave / (NW / 2), st_part = wave % (NW / 2);
-    const float *st_src = (st_kind == 0 ? LSE : Dvec) + (int64_t)bh * Nq;
+    auto st_base = [&](int bh_) { return (st_kind == 0 ? LSE : Dvec) + (int64_t)bh_ * Nq; };
     float sreg = 0.f;
     int st_row0 = 0;
-    auto fetch_stats = [&](int qt) __attribute__((always_inline)) {
+    auto fetch_stats = [&](int qt, const float *src) __attribute__((always_inline)) {
         st_row0 = qt * BQ + 64 * st_part;
-        sreg = st_src[min(st_row0 + lane, Nq - 1)];
+        sreg = src[min(st_row0 + lane, Nq - 1)];
     };
-    // copy jb of this wave's share of the Q and dO rows of tile qt, into stage s
-    auto fetch_copy = [&](int qt, int s, int jb) __attribute__((always_inline)) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 in the clobber list: see the kernel's notes
+    // copy jb of this wave's share of the Q and dO rows of tile qt (of the head
+    // at Qb, dOb), into stage s
+    auto fetch_copy = [&](int qt, int s, int jb, const uint16_t *Qb, const uint16_t *dOb)
+        __attribute__((always_inline)) {
         const int grow = min(qt * BQ + cp_row + 16 * jb, Nq - 1);  // rows past Nq re-read row Nq - 1 (zero weight)
         const uint32_t off = (uint32_t)grow * (uint32_t)(D * 2) + cp_col;  // bytes from the head's first row
         const uint32_t dq = (uint32_t)(2 * s * TILE + (wave + NW * jb) * 1024);
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // M0 in the clobber list: see the kernel's notes
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(Qh), "s"(dq)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(Qb), "s"(dq)
                      : "memory", "m0");
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(dOh),
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(dOb),
                      "s"(dq + (uint32_t)TILE)
                      : "memory", "m0");
-#pragma clang diagnostic pop
     };
+    // the K and V rows of key block kt_ of head bh_ into the KV region: 32
+    // blocks of 4 rows per tensor, 8 per wave; rows past Nk re-read row Nk - 1
+    // (their results are never stored)
+    auto fetch_kv = [&](int bh_, int kt_) __attribute__((always_inline)) {
+        const uint16_t *Kb = static_cast<const uint16_t *>(K) + (int64_t)bh_ * Nk * D;
+        const uint16_t *Vb = static_cast<const uint16_t *>(V) + (int64_t)bh_ * Nk * D;
+#pragma unroll
+        for (int jb = 0; jb < BKC / 16; ++jb) {
+            const int grow = min(kt_ * BKC + cp_row + 16 * jb, Nk - 1);
+            const uint32_t off = (uint32_t)grow * (uint32_t)(D * 2) + cp_col;
+            const uint32_t dk = (uint32_t)(KV + (wave + NW * jb) * 1024);
+            asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(Kb),
+                         "s"(dk)
+                         : "memory", "m0");
+            asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(Vb),
+                         "s"(dk + (uint32_t)KVB)
+                         : "memory", "m0");
+        }
+    };
+#pragma clang diagnostic pop
     // The statistics of the last fetch into stage s, once their loads landed
     // (a store in every wave: no branch sinks the loads to the end of the
     // step).  Rows past Nq get LSE = inf (P = 0) and D = 0.
@@ -579,19 +603,7 @@ void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, 
     };
 
     f32x16_t dvT[NDB], dkT[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) { dvT[db] = f32x16_t{}; dkT[db] = f32x16_t{}; }
-
-    if (qt_begin < n_qt) {
-        fetch_stats(qt_begin);
-#pragma unroll
-        for (int jb = 0; jb < NCP; ++jb) fetch_copy(qt_begin, 0, jb);
-        wait_vmem();
-        put_stats(0);
-    }
-    wait_vmem();
-    __syncthreads();
-    mfma_wait<3>();  // the zeroed accumulators, before mfma_acc reads them
+    u32x4_t kf[NKS], vn[NKS];  // K and -V fragments: lane = key, k = head-dim index 16*ks + 8*g + v
 
     // Position of group G (16 products) in the step's order A0 A1 B0 A2 B1 ... B(NB-1):
     // is it an A group, and of which block.
@@ -606,7 +618,8 @@ void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, 
     // tile's copies go into the other stage, which every wave finished reading
     // before this step's barrier.  MASK: apply the causal mask (the tile
     // reaches this workgroup's keys).
-    auto step_pipe = [&](int qt, int s, int qn, auto mask_c) __attribute__((always_inline)) {
+    auto step_pipe = [&](int qt, int s, int qn, const uint16_t *Qn, const uint16_t *dOn, auto mask_c)
+        __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_c)::value;
         const uint32_t sb = (uint32_t)(2 * s * TILE), stb = (uint32_t)(s * 8 * BQ);
         uint32_t ao[NKS], to[NDB][2];
@@ -688,7 +701,7 @@ void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, 
             mm(i);
             if constexpr (i + LEAD < NP) rd(i + LEAD);
             // the next tile's copies, during the first products
-            if constexpr (i >= 1 && i <= NCP) fetch_copy(qn, s ^ 1, i - 1);
+            if constexpr (i >= 1 && i <= NCP) fetch_copy(qn, s ^ 1, i - 1, Qn, dOn);
             static_for<NB>([&](auto bc) __attribute__((always_inline)) {
                 constexpr int b = decltype(bc)::value;
                 // block b's D, ten products ahead of its first dP product
@@ -705,45 +718,100 @@ void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, 
         });
     };
 
-    auto step = [&](int qt, auto mask_c) __attribute__((always_inline)) {
-        const int s = (qt - qt_begin) & 1;
-        // (past the last tile the copy repeats this one into the idle stage, so
-        // every step issues the same copies and no branch splits the step)
-        const int qn = qt + 1 < n_qt ? qt + 1 : qt;
-        fetch_stats(qn);
-        step_pipe(qt, s, qn, mask_c);
-        // the next tile's copies and statistics have landed: publish them
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        put_stats(s ^ 1);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-    };
-    // Causal: the first tiles reach this workgroup's keys and take the masked
-    // program, in a loop of their own (one loop holding both programs needs
-    // more registers than the file has); the rest need no mask.
-    const int qt_mask_end = CAUSAL ? min(n_qt, (k0 + BKC + BQ - 1) / BQ) : qt_begin;
-    for (int qt = qt_begin; qt < qt_mask_end; ++qt) step(qt, std::true_type{});
-    for (int qt = qt_mask_end; qt < n_qt; ++qt) step(qt, std::false_type{});
+    int L = item_of(0);
+    int base = 0;  // the stage of the current item's first tile
+    if (L >= 0) {  // the first item's K/V rows, first tile and its statistics
+        decode(L, bh, kt);
+        const int qb0 = CAUSAL ? min(kt * BKC / BQ, n_qt) : 0;
+        fetch_kv(bh, kt);
+        if (qb0 < n_qt) {
+            fetch_stats(qb0, st_base(bh));
+#pragma unroll
+            for (int jb = 0; jb < NCP; ++jb) fetch_copy(qb0, 0, jb, q_base(bh), do_base(bh));
+            wait_vmem();
+            put_stats(0);
+        }
+        wait_vmem();
+        __syncthreads();
+    }
+    for (int it = 0; L >= 0; ++it) {
+        const int Ln = item_of(it + 1);
+        int bhn = 0, ktn = 0;
+        decode(L, bh, kt);
+        if (Ln >= 0) decode(Ln, bhn, ktn);
+        q_head = (int64_t)bh * Nq * D;
+        k_head = (int64_t)bh * Nk * D;
+        k0 = kt * BKC;
+        kw = k0 + wave * 32 + l32;  // this lane's key
+        kwg = kw - 4 * g;           // the key less the lane's 4g offset in the score registers' row order
+        qt_begin = CAUSAL ? min(k0 / BQ, n_qt) : 0;  // earlier rows see none of these keys
+        const uint16_t *Qh = q_base(bh), *dOh = do_base(bh);
+        const float *sth = st_base(bh);
+        // the next item's first tile (rows 0: it is non-causal)
+        const uint16_t *Qx = Ln >= 0 ? q_base(bhn) : Qh, *dOx = Ln >= 0 ? do_base(bhn) : dOh;
+        const float *stx = Ln >= 0 ? st_base(bhn) : sth;
 
-    // the accumulators were last written by matrix products the compiler does
-    // not see (mfma_acc): give them their result latency before any read
-    mfma_drain();
-    if (kw < Nk) {
-        // dK = scale * dK^T (accumulated negated), dV = dV^T: lane = key,
-        // register r -> head dim 32db + 8*(r/4) + 4*g + r%4
-        const int64_t row = k_head + (int64_t)kw * D;
-        const float nscale = -scale;
+        // K and -V fragments from the KV region (the swizzle depends on the
+        // row's low four bits, so the wave's rows 32 wave + l32 sit at the A
+        // operand offsets plus 8 KiB per wave); every wave holds them before
+        // the region takes the next item's rows
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int ks = 0; ks < NKS; ++ks) {
+            kf[ks] = *reinterpret_cast<const u32x4_t *>(lds + KV + 8192 * wave + a_off[ks]);
+            vn[ks] = *reinterpret_cast<const u32x4_t *>(lds + KV + KVB + 8192 * wave + a_off[ks]) ^ 0x80008000u;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const int col = db * 32 + 8 * rq + 4 * g;
-                store4<E>(dK, row + col, dkT[db][4 * rq] * nscale, dkT[db][4 * rq + 1] * nscale,
-                          dkT[db][4 * rq + 2] * nscale, dkT[db][4 * rq + 3] * nscale);
-                store4<E>(dV, row + col, dvT[db][4 * rq], dvT[db][4 * rq + 1], dvT[db][4 * rq + 2],
-                          dvT[db][4 * rq + 3]);
-            }
+        for (int db = 0; db < NDB; ++db) { dvT[db] = f32x16_t{}; dkT[db] = f32x16_t{}; }
+        mfma_wait<3>();  // the zeroed accumulators, before mfma_acc reads them
+
+        auto step = [&](int qt, auto mask_c) __attribute__((always_inline)) {
+            const int s = (base + qt - qt_begin) & 1;
+            const bool last = qt + 1 == n_qt;
+            if (last && Ln >= 0) fetch_kv(bhn, ktn);  // the next item's rows, beside this last step
+            // the next tile, or past the last one the next item's first tile (or,
+            // with no next item, this tile again into the idle stage, so every
+            // step issues the same copies and no branch splits the step)
+            const int qn = last ? (Ln >= 0 ? 0 : qt) : qt + 1;
+            fetch_stats(qn, last ? stx : sth);
+            step_pipe(qt, s, qn, last ? Qx : Qh, last ? dOx : dOh, mask_c);
+            // the next tile's copies and statistics have landed: publish them
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            put_stats(s ^ 1);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        // Causal: the first tiles reach this workgroup's keys and take the masked
+        // program, in a loop of their own (one loop holding both programs needs
+        // more registers than the file has); the rest need no mask.
+        const int qt_mask_end = CAUSAL ? min(n_qt, (k0 + BKC + BQ - 1) / BQ) : qt_begin;
+        for (int qt = qt_begin; qt < qt_mask_end; ++qt) step(qt, std::true_type{});
+        for (int qt = qt_mask_end; qt < n_qt; ++qt) step(qt, std::false_type{});
+        base = (base + n_qt - qt_begin) & 1;
+
+        // the accumulators were last written by matrix products the compiler does
+        // not see (mfma_acc): give them their result latency before any read
+        mfma_drain();
+        if (kw < Nk) {
+            // dK = scale * dK^T (accumulated negated), dV = dV^T: lane = key,
+            // register r -> head dim 32db + 8*(r/4) + 4*g + r%4
+            const int64_t row = k_head + (int64_t)kw * D;
+            const float nscale = -scale;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int col = db * 32 + 8 * rq + 4 * g;
+                    store4<E>(dK, row + col, dkT[db][4 * rq] * nscale, dkT[db][4 * rq + 1] * nscale,
+                              dkT[db][4 * rq + 2] * nscale, dkT[db][4 * rq + 3] * nscale);
+                    store4<E>(dV, row + col, dvT[db][4 * rq], dvT[db][4 * rq + 1], dvT[db][4 * rq + 2],
+                              dvT[db][4 * rq + 3]);
+                }
+        }
+        L = Ln;
     }
 }
 
@@ -1275,7 +1343,11 @@ static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
         const int n_kt = (a.Nk + 127) / 128;
         if constexpr (D == 128 && E != ELT_F32 && FA_DKDV_KV) {
             if (!drop) {
-                hipLaunchKernelGGL((bwd_dkdv_kv_kernel<E, CAUSAL>), dim3(BH * n_kt), dim3(256), 0, st, a.Q, a.K, a.V,
+                // causal: one key block per workgroup; otherwise one persistent
+                // workgroup per compute unit walks the blocks
+                const int items = BH * n_kt;
+                const int grid = CAUSAL ? items : std::min(items, compute_units());
+                hipLaunchKernelGGL((bwd_dkdv_kv_kernel<E, CAUSAL>), dim3(grid), dim3(256), 0, st, a.Q, a.K, a.V,
                                    a.dO, a.LSE, a.Dvec, a.dK, a.dV, BH, a.Nq, a.Nk, a.scale, sl2, n_kt);
                 const hipError_t e = hipGetLastError();
                 if (e != hipSuccess) return e;
@@ -1330,7 +1402,8 @@ const char *describe_bwd() {
            "128 keys, 64-row query steps (128 at d=64), double-buffered Q/dO, transposed LDS reads> -> "
            "bwd_dq_kernel<D, 8 waves x 32 rows, 64-key tiles (128 at d=64)>; d=128 16-bit without dropout: "
            "bwd_dq_kv_kernel<4 waves, one per SIMD, 64 rows each, Q^T and dQ accumulators in AGPRs, 64-key tiles "
-           "as a fixed program, forms D itself> -> bwd_dkdv_kv_kernel<4 waves, one per SIMD, 32 keys each with K/V "
+           "as a fixed program, forms D itself> -> bwd_dkdv_kv_kernel<4 waves, one per SIMD, persistent (non-causal), "
+           "32 keys each with K/V "
            "fragments in registers, dV/dK accumulators in AGPRs, 64-row steps as a fixed product/softmax program>; "
            "no atomics";
 }

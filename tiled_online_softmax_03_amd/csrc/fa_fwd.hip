@@ -968,7 +968,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(SplitOut part, int G, in
 // Compute units of the current device (cached per device; every MI355X has
 // 256).  Callers on several host threads may race to fill an entry: they
 // store the same value, through an atomic.
-static int compute_units() {
+int compute_units() {
     static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

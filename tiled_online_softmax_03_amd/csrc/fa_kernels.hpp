@@ -39,6 +39,8 @@ struct BwdArgs {
     Dropout drop{0u, 0u, 0u, 1.f};  // t = 0: no dropout
 };
 
+// Compute units of the current device (the grid of the persistent kernels).
+int compute_units();
 hipError_t launch_fwd(const FwdArgs &a);
 int fwd_key_tile(int d);  // keys per tile of the forward's key loop for head dim d
 int fwd_query_tile();  // query rows per forward workgroup
