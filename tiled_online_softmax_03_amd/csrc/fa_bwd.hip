@@ -1010,6 +1010,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const void *__restrict__ Q,
 // products (A) and 16 dQ products (B), ordered A0 A1 B0 B1: block 0's
 // softmax gradient runs beside A1, block 1's beside B0 and the first half of
 // B1 (B1's first eight products need only keys 0..15 of the block).
+// Non-causal launches are persistent: one workgroup per compute unit walks the
+// query tiles, and each tile's Q rows (read from LDS into AGPRs) and first K/V
+// tile reach LDS while the tile before it computes.
 template <int E, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, const void *__restrict__ V,
@@ -1024,48 +1027,147 @@ void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, co
     constexpr int NP = 96;            // matrix products per step
     constexpr int LEAD = FA_KV_LEAD, NSLOT = LEAD + 1;
     static_assert(E != ELT_F32, "16-bit operands are copied global -> LDS as they are");
-    // stage s: K at 2 s TILE, V at (2 s + 1) TILE
-    __shared__ __attribute__((aligned(16))) unsigned char lds[4 * TILE];
+    // stage s: K at 2 s TILE, V at (2 s + 1) TILE; the workgroup's Q tile (BR
+    // rows, tile_off layout) at QS, copied while the item before it computes
+    constexpr int QS = 4 * TILE;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[QS + BR * D * 2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g = lane >> 5;
 
-    int bh, qt;
-    if constexpr (CAUSAL) {
-        const int L = blockIdx.x;  // longest rows first
-        qt = n_qt - 1 - L / BH;
-        bh = L % BH;
-    } else {
-        const int L = xcd_remap(blockIdx.x, gridDim.x);
-        bh = L / n_qt;
-        qt = L % n_qt;
+    // Work items are query tiles.  Causal: one per workgroup, the longest rows
+    // first.  Otherwise the workgroups are persistent: workgroup w takes the
+    // tiles it * gridDim.x + xcd_remap(w), and each item's Q tile and first
+    // K/V tile are copied while the item before it computes.
+    const int n_items = BH * n_qt;
+    auto item_of = [&](int it) -> int {
+        if constexpr (CAUSAL) return it == 0 ? (int)blockIdx.x : -1;
+        const int L = it * (int)gridDim.x + xcd_remap(blockIdx.x, gridDim.x);
+        return L < n_items ? L : -1;
+    };
+    auto decode = [&](int L, int &bh_, int &qt_) __attribute__((always_inline)) {
+        if constexpr (CAUSAL) {
+            qt_ = n_qt - 1 - L / BH;
+            bh_ = L % BH;
+        } else {
+            bh_ = L / n_qt;
+            qt_ = L % n_qt;
+        }
+    };
+    auto k_tiles = [&](int qt_) {  // key tiles of query tile qt_
+        const int k_end = CAUSAL ? min(Nk, min(qt_ * BR + BR, Nq)) : Nk;
+        return (k_end + BC - 1) / BC;
+    };
+
+    // Per-lane LDS byte offsets in a tile (tile_off<128> layout):
+    //  a_off[ks]: the A operand (key row l32 of a 32-key block, head dims
+    //  16ks + 8g .. +7); t_off[db][hf]: the transposed read of key rows
+    //  4g + j/4 + 8 hf, head dims 32 db + 16 ((lane / 16) % 2) + 4 (j % 4).
+    uint32_t a_off[NKS], t_off[NDB][2];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) a_off[ks] = 2u * (uint32_t)tile_off<D>(l32, 16 * ks + 8 * g);
+    {
+        const int j = lane & 15;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                t_off[db][hf] = 2u * (uint32_t)tile_off<D>(4 * g + (j >> 2) + 8 * hf, 32 * db + 16 * ((lane >> 4) & 1) + 4 * (j & 3));
     }
-    const int64_t q_head = (int64_t)bh * Nq * D;
-    const int64_t k_head = (int64_t)bh * Nk * D;
-    const int q_w0 = qt * BR + 64 * wave;  // first row of this wave
 
-    int k_end = Nk;
-    if constexpr (CAUSAL) k_end = min(Nk, min(qt * BR + BR, Nq));
-    const int n_kt = (k_end + BC - 1) / BC;
+    // Copies global -> LDS in blocks of 4 rows (1 KiB), block b = wave + 4 jb
+    // (the same swizzle for every jb).  A K/V tile: NCP blocks per wave per
+    // tensor, key rows past Nk re-read row Nk - 1 (their scores are masked).
+    // The Q tile: BR / 16 blocks per wave, rows past Nq re-read row Nq - 1
+    // (never stored).
+    const int cp_row = wave * 4 + lane / 16;  // + 16 jb
+    const uint32_t cp_col = (uint32_t)((lane & 15) ^ swz<D>(cp_row)) * 16u;
+    auto k_base = [&](int bh_) { return static_cast<const uint16_t *>(K) + (int64_t)bh_ * Nk * D; };
+    auto v_base = [&](int bh_) { return static_cast<const uint16_t *>(V) + (int64_t)bh_ * Nk * D; };
+    auto q_base = [&](int bh_) { return static_cast<const uint16_t *>(Q) + (int64_t)bh_ * Nq * D; };
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 in the clobber list: see the kernel's notes
+    auto fetch_copy = [&](int kt, int s, int jb, const uint16_t *Kb, const uint16_t *Vb) __attribute__((always_inline)) {
+        const int grow = min(kt * BC + cp_row + 16 * jb, Nk - 1);
+        const uint32_t off = (uint32_t)grow * (uint32_t)(D * 2) + cp_col;  // bytes from the head's first row
+        const uint32_t dk = (uint32_t)(2 * s * TILE + (wave + NW * jb) * 1024);
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(Kb), "s"(dk)
+                     : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(Vb),
+                     "s"(dk + (uint32_t)TILE)
+                     : "memory", "m0");
+    };
+    auto copy_q = [&](int q0, const uint16_t *Qb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jb = 0; jb < BR / 16; ++jb) {
+            const int grow = min(q0 + cp_row + 16 * jb, Nq - 1);
+            const uint32_t off = (uint32_t)grow * (uint32_t)(D * 2) + cp_col;
+            const uint32_t dq = (uint32_t)(QS + (wave + NW * jb) * 1024);
+            asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(Qb), "s"(dq)
+                         : "memory", "m0");
+        }
+    };
+#pragma clang diagnostic pop
 
-    // Q^T and dO^T fragments of both row blocks (B operands, k = head-dim index
-    // 16*ks + 8*g + v, lane = row q_w0 + 32 r + l32) and the rows' statistics.
-    // This pass runs first and forms D = rowsum(dO * O) itself ([RA] section
-    // 04's D term): each lane adds its 64 head dims of the row in fp32, the
-    // permlane32 swap adds the two halves (the same sum in both lanes), and
-    // the g = 0 lanes store it for the dK/dV pass that follows.
+    // the current item (updated at the top of the item loop)
+    int bh = 0, qt = 0, q_w0 = 0, n_kt = 0;
+    int64_t q_head = 0;
     u32x4_t qf[2][NKS], df[2][NKS];
     float lse2[2], dv[2];
+    int klim[2];
+    f32x16_t dqT[2][NDB];
+    int base = 0;  // the stage of the current item's first key tile
+    int L = item_of(0);
+    if (L >= 0) {  // the first item's Q tile and first K/V tile
+        int bh0, qt0;
+        decode(L, bh0, qt0);
+        copy_q(qt0 * BR, q_base(bh0));
+        if (k_tiles(qt0) > 0) {
+#pragma unroll
+            for (int jb = 0; jb < NCP; ++jb) fetch_copy(0, 0, jb, k_base(bh0), v_base(bh0));
+        }
+        wait_vmem();
+        __syncthreads();
+    }
+    for (int it = 0; L >= 0; ++it) {
+    const int Ln = item_of(it + 1);
+    int bhn = 0, qtn = 0;
+    decode(L, bh, qt);
+    if (Ln >= 0) decode(Ln, bhn, qtn);
+    q_head = (int64_t)bh * Nq * D;
+    q_w0 = qt * BR + 64 * wave;  // first row of this wave
+    n_kt = k_tiles(qt);
+    const uint16_t *Kh = k_base(bh), *Vh = v_base(bh);
+    // the next item's first tile (non-causal: every item has n_kt >= 1, and its
+    // last step copies it)
+    const uint16_t *Kx = Ln >= 0 ? k_base(bhn) : Kh, *Vx = Ln >= 0 ? v_base(bhn) : Vh;
+
+    // Q^T fragments (B operands, k = head-dim index 16*ks + 8*g + v, lane = row
+    // q_w0 + 32 r + l32) from the Q tile into AGPRs: the swizzle depends on the
+    // row's low four bits, so they sit at the A operand offsets plus 256 bytes
+    // per row of 64 wave + 32 r (the per-wave part opaque per item, so the sums
+    // are formed here).
+    {
+        uint32_t qb = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char *)lds) +
+                      (uint32_t)(QS + 64 * 256 * wave);
+        asm volatile("" : "+s"(qb));
+        uint32_t qa[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qa[ks] = qb + a_off[ks];
+        lds_read_agpr(qf, qa);
+    }
+    // dO^T fragments of both row blocks and the rows' statistics.  This pass
+    // runs first and forms D = rowsum(dO * O) itself ([RA] section 04's D
+    // term): each lane adds its 64 head dims of the row in fp32, the permlane32
+    // swap adds the two halves (the same sum in both lanes), and the g = 0
+    // lanes store it for the dK/dV pass that follows.
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int q = q_w0 + 32 * r + l32;
         const int q_ld = q < Nq ? q : Nq - 1;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            qf[r][ks] = load8_operand<E>(Q, q_head + (int64_t)q_ld * D + 16 * ks + 8 * g);
-            df[r][ks] = load8_operand<E>(dO, q_head + (int64_t)q_ld * D + 16 * ks + 8 * g);
-        }
+        for (int ks = 0; ks < NKS; ++ks) df[r][ks] = load8_operand<E>(dO, q_head + (int64_t)q_ld * D + 16 * ks + 8 * g);
         lse2[r] = LSE[(int64_t)bh * Nq + q_ld] * kLog2e;
         float acc = 0.f;
 #pragma unroll
@@ -1084,66 +1186,16 @@ void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, co
     }
     // last key each lane's rows see (past Nk, or causal past the row), less
     // the lane's 4g offset in the score registers' key order
-    int klim[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) klim[r] = (CAUSAL ? min(q_w0 + 32 * r + l32, Nk - 1) : Nk - 1) - 4 * g;
+    // every wave holds its Q^T: the tile's space takes the next item's
+    __syncthreads();
+    if (Ln >= 0) copy_q(qtn * BR, q_base(bhn));
 
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            qf[r][ks] = to_agpr(qf[r][ks]);
-        }
-
-    // Per-lane LDS byte offsets in a tile (tile_off<128> layout):
-    //  a_off[ks]: the A operand (key row l32 of a 32-key block, head dims
-    //  16ks + 8g .. +7); t_off[db][hf]: the transposed read of key rows
-    //  4g + j/4 + 8 hf, head dims 32 db + 16 ((lane / 16) % 2) + 4 (j % 4).
-    uint32_t a_off[NKS], t_off[NDB][2];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) a_off[ks] = 2u * (uint32_t)tile_off<D>(l32, 16 * ks + 8 * g);
-    {
-        const int j = lane & 15;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-                t_off[db][hf] = 2u * (uint32_t)tile_off<D>(4 * g + (j >> 2) + 8 * hf, 32 * db + 16 * ((lane >> 4) & 1) + 4 * (j & 3));
-    }
-
-    // Copies of a tile: blocks of 4 key rows (1 KiB), NCP per wave per tensor,
-    // block b = wave + 4 jb (the same swizzle for every jb); rows past Nk
-    // re-read row Nk - 1 (their scores are masked).
-    const uint16_t *Kh = static_cast<const uint16_t *>(K) + k_head;
-    const uint16_t *Vh = static_cast<const uint16_t *>(V) + k_head;
-    const int cp_row = wave * 4 + lane / 16;  // + 16 jb
-    const uint32_t cp_col = (uint32_t)((lane & 15) ^ swz<D>(cp_row)) * 16u;
-    auto fetch_copy = [&](int kt, int s, int jb) __attribute__((always_inline)) {
-        const int grow = min(kt * BC + cp_row + 16 * jb, Nk - 1);
-        const uint32_t off = (uint32_t)grow * (uint32_t)(D * 2) + cp_col;  // bytes from the head's first row
-        const uint32_t dk = (uint32_t)(2 * s * TILE + (wave + NW * jb) * 1024);
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // M0 in the clobber list: see the kernel's notes
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(Kh), "s"(dk)
-                     : "memory", "m0");
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(Vh),
-                     "s"(dk + (uint32_t)TILE)
-                     : "memory", "m0");
-#pragma clang diagnostic pop
-    };
-
-    f32x16_t dqT[2][NDB];
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) dqT[r][db] = f32x16_t{};
-
-    if (n_kt > 0) {
-#pragma unroll
-        for (int jb = 0; jb < NCP; ++jb) fetch_copy(0, 0, jb);
-    }
-    wait_vmem();
-    __syncthreads();
     mfma_wait<3>();  // the zeroed accumulators, before mfma_acc reads them
 
     // One key tile in stage s: products 0..31 A(block 0), 32..63 A(block 1),
@@ -1151,7 +1203,8 @@ void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, co
     // (i % 32) / 4, tensor w = (i % 4) / 2 (K: S^T, V: dP^T), row block i % 2.
     // B product j = (i - 64) % 16: k-step h = j / 8, db = (j % 8) / 2, row block j % 2.
     // MASK: apply the mask of keys past Nk and, causal, of keys after the row.
-    auto step_pipe = [&](int kt, int s, int kn, auto mask_c) __attribute__((always_inline)) {
+    auto step_pipe = [&](int kt, int s, int kn, const uint16_t *Kn, const uint16_t *Vn, auto mask_c)
+        __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_c)::value;
         const uint32_t sb = (uint32_t)(2 * s * TILE);
         uint32_t ao[NKS], to[NDB][2];
@@ -1254,7 +1307,7 @@ void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, co
                 rd(m, perm(m));
                 rd(m + 1, perm(m + 1));
             }
-            if constexpr (n >= 1 && n <= NCP) fetch_copy(kn, s ^ 1, n - 1);
+            if constexpr (n >= 1 && n <= NCP) fetch_copy(kn, s ^ 1, n - 1, Kn, Vn);
             if constexpr (!MASK) {
                 // block 0's softmax beside A(block 1) (32 units in 32 slots);
                 // block 1's beside B(block 0) and the first half of B(block 1):
@@ -1274,8 +1327,11 @@ void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, co
     };
 
     auto step = [&](int kt, auto mask_c) __attribute__((always_inline)) {
-        const int kn = kt + 1 < n_kt ? kt + 1 : kt;
-        step_pipe(kt, kt & 1, kn, mask_c);
+        const bool last = kt + 1 == n_kt;
+        // the next tile, or past the last one the next item's first tile (with
+        // no next item, this tile again into the idle stage)
+        const int kn = last ? (Ln >= 0 ? 0 : kt) : kt + 1;
+        step_pipe(kt, (base + kt) & 1, kn, last ? Kx : Kh, last ? Vx : Vh, mask_c);
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -1289,6 +1345,13 @@ void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, co
     n_full = min(n_full, n_kt);
     for (int kt = 0; kt < n_full; ++kt) step(kt, std::false_type{});
     for (int kt = n_full; kt < n_kt; ++kt) step(kt, std::true_type{});
+    base = (base + n_kt) & 1;
+    if (n_kt == 0 && Ln >= 0) {  // no step to copy the next item's first tile
+#pragma unroll
+        for (int jb = 0; jb < NCP; ++jb) fetch_copy(0, base, jb, Kx, Vx);
+        wait_vmem();
+        __syncthreads();
+    }
 
     mfma_drain();  // mfma_acc results, before they are read
     // dQ = scale * (dQ^T)^T: lane = row, register r -> head dim 32db + 8*(r/4) + 4*g + r%4
@@ -1305,6 +1368,8 @@ void bwd_dq_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, co
                               dqT[r][db][4 * rq + 1] * scale, dqT[r][db][4 * rq + 2] * scale,
                               dqT[r][db][4 * rq + 3] * scale);
         }
+    }
+    L = Ln;
     }
 }
 
@@ -1327,8 +1392,11 @@ static hipError_t launch_bwd_t(const BwdArgs &a, int stage) {
         if (stage < 0 || stage == 0) {
             const int n_qt = (a.Nq + 255) / 256;
             if constexpr (D == 128 && E != ELT_F32)
-                hipLaunchKernelGGL((bwd_dq_kv_kernel<E, CAUSAL>), dim3(BH * n_qt), dim3(256), 0, st, a.Q, a.K, a.V,
-                                   a.O, a.dO, a.LSE, a.Dvec, a.dQ, BH, a.Nq, a.Nk, a.scale, sl2, n_qt);
+                // causal: one query tile per workgroup; otherwise one persistent
+                // workgroup per compute unit walks the tiles
+                hipLaunchKernelGGL((bwd_dq_kv_kernel<E, CAUSAL>),
+                                   dim3(CAUSAL ? BH * n_qt : std::min(BH * n_qt, compute_units())), dim3(256), 0, st,
+                                   a.Q, a.K, a.V, a.O, a.dO, a.LSE, a.Dvec, a.dQ, BH, a.Nq, a.Nk, a.scale, sl2, n_qt);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -1401,7 +1469,8 @@ const char *describe_bwd() {
     return "bwd_pre_kernel (D=rowsum(dO*O)) -> bwd_dkdv_kernel<D, 8 waves = 4 key groups x 2 query halves, "
            "128 keys, 64-row query steps (128 at d=64), double-buffered Q/dO, transposed LDS reads> -> "
            "bwd_dq_kernel<D, 8 waves x 32 rows, 64-key tiles (128 at d=64)>; d=128 16-bit without dropout: "
-           "bwd_dq_kv_kernel<4 waves, one per SIMD, 64 rows each, Q^T and dQ accumulators in AGPRs, 64-key tiles "
+           "bwd_dq_kv_kernel<4 waves, one per SIMD, persistent (non-causal), 64 rows each, Q^T and dQ "
+           "accumulators in AGPRs, 64-key tiles "
            "as a fixed program, forms D itself> -> bwd_dkdv_kv_kernel<4 waves, one per SIMD, persistent (non-causal), "
            "32 keys each with K/V "
            "fragments in registers, dV/dK accumulators in AGPRs, 64-row steps as a fixed product/softmax program>; "
