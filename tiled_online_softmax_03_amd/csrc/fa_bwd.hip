@@ -518,7 +518,7 @@ void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, 
     const int n_qt = (Nq + BQ - 1) / BQ;
     // the current item (updated at the top of the item loop)
     int bh = 0, kt = 0, k0 = 0, kw = 0, kwg = 0, qt_begin = 0;
-    int64_t q_head = 0, k_head = 0;
+    int64_t k_head = 0;
 
     // Per-lane LDS byte offsets in a tile (tile_off<128> layout):
     //  a_off[ks]: the A operand (row l32, head dims 16ks + 8g .. +7);
@@ -739,7 +739,6 @@ void bwd_dkdv_kv_kernel(const void *__restrict__ Q, const void *__restrict__ K, 
         int bhn = 0, ktn = 0;
         decode(L, bh, kt);
         if (Ln >= 0) decode(Ln, bhn, ktn);
-        q_head = (int64_t)bh * Nq * D;
         k_head = (int64_t)bh * Nk * D;
         k0 = kt * BKC;
         kw = k0 + wave * 32 + l32;  // this lane's key
